@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: values
+worked out by hand (tests/golden/hand_blocks.json), closed-form values of the
+OCP FP4 E2M1 / FP8 E4M3FN formats, independent library routines (torch's
+float8_e4m3fn and bfloat16 casts, numpy's matmul), and exact rational
+arithmetic (fractions.Fraction) on small inputs.  Together they fail on a
+dropped term, a wrong sign, a wrong nibble or scale index, or a transposed
+operand anywhere in the oracle.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from nvfp4_weight_only_02_amd import inputs
+
+# ---------------------------------------------------------------------------
+# independent decoders used as pins
+
+
+def e2m1_from_fields(code: int) -> Fraction:
+    """E2M1 from its bit fields: sign bit 3, exponent bits 2..1 (bias 1),
+    mantissa bit 0; exponent 0 is subnormal M/2."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    v = Fraction(m, 2) if e == 0 else (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+    return -v if s else v
+
+
+def e4m3_torch(byte_values) -> np.ndarray:
+    t = torch.tensor(np.asarray(byte_values, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+E4M3_ALL = e4m3_torch(np.arange(256))
+E4M3_POS_FR = [Fraction(float(E4M3_ALL[b])) for b in range(0x7F)]  # bytes 0x00..0x7E
+E2M1_POS_FR = [e2m1_from_fields(c) for c in range(8)]
+
+
+def decode_dense_independent(codes, scales, g):
+    """Dense fp64 W from the canonical bytes without the oracle: nibbles by
+    numpy bit ops, magnitudes from the bit fields, scales via torch."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    nib = np.empty((N, K), dtype=np.int64)
+    nib[:, 0::2] = codes & 15
+    nib[:, 1::2] = codes >> 4
+    table = np.array([float(e2m1_from_fields(c)) for c in range(16)])
+    sc = e4m3_torch(scales.reshape(-1)).reshape(scales.shape)
+    return table[nib] * np.repeat(sc, 16, axis=1) * np.float64(np.float32(g))
+
+
+def nearest_even(v: Fraction, grid):
+    """Index of the nearest grid point to v (grid ascending), ties to even index."""
+    best, best_err = 0, abs(v - grid[0])
+    for i in range(1, len(grid)):
+        err = abs(v - grid[i])
+        if err < best_err or (err == best_err and i % 2 == 0):
+            best, best_err = i, err
+    return best
+
+
+def nearest_f32(v: Fraction) -> np.float32:
+    """Correctly rounded (ties to even) fp32 of a non-negative rational."""
+    c = np.float32(float(v))
+    cands = [np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))]
+    best = None
+    for x in cands:
+        err = abs(Fraction(float(x)) - v)
+        key = (err, int(np.array(x).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, x)
+    return np.float32(best[1])
+
+
+def exact_quantize(W: np.ndarray):
+    """The input recipe in exact rational arithmetic."""
+    N, K = W.shape
+    amax = max((abs(Fraction(float(w))) for w in W.reshape(-1)), default=Fraction(0))
+    g = nearest_f32(amax / 2688)
+    gF = Fraction(float(g))
+    codes = np.zeros((N, K // 2), dtype=np.uint8)
+    scales = np.zeros((N, K // 16), dtype=np.uint8)
+    for r in range(N):
+        for b in range(K // 16):
+            blk = [Fraction(float(w)) for w in W[r, 16 * b:16 * b + 16]]
+            if gF == 0:
+                s = 0
+            else:
+                v = max(abs(x) for x in blk) / (6 * gF)
+                s = 0x7E if v >= 448 else nearest_even(v, E4M3_POS_FR)
+            scales[r, b] = s
+            d = E4M3_POS_FR[s] * gF
+            for i, x in enumerate(blk):
+                k = 16 * b + i
+                mag = 0 if d == 0 else (7 if abs(x) / d >= 6 else nearest_even(abs(x) / d, E2M1_POS_FR))
+                code = mag | (8 if np.signbit(W[r, k]) else 0)
+                codes[r, k // 2] |= code if k % 2 == 0 else code << 4
+    return codes, scales, float(g)
+
+
+def random_packed(rng, N, K, scale_max=0x7E):
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, scale_max + 1, size=(N, K // 16), dtype=np.uint8)
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# format tables
+
+
+def test_e2m1_table_closed_values():
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for c in range(16):
+        assert O.e2m1(c) == float(e2m1_from_fields(c))
+        assert abs(O.e2m1(c)) == mags[c & 7]
+        assert np.signbit(O.e2m1(c)) == bool(c & 8)
+
+
+def test_e4m3_table_matches_torch_float8():
+    for b in range(256):
+        got = O.e4m3(b)
+        if (b & 0x7F) == 0x7F:
+            assert np.isnan(got) and np.isnan(E4M3_ALL[b])
+        else:
+            assert got == E4M3_ALL[b], hex(b)
+
+
+def test_e4m3_special_values():
+    assert O.e4m3(0x7E) == 448.0
+    assert O.e4m3(0x01) == 2.0 ** -9
+    assert O.e4m3(0x08) == 2.0 ** -6
+    assert O.e4m3(0x38) == 1.0
+    assert O.e4m3(0x40) == 2.0
+    assert O.e4m3(0xFE) == -448.0
+    assert O.e4m3(0x80) == 0.0 and np.signbit(O.e4m3(0x80))
+    vals = [O.e4m3(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+
+
+# ---------------------------------------------------------------------------
+# rounding used by the quantiser and the output
+
+
+def test_e2m1_rne_hand(golden):
+    case = golden["e2m1_rne_ties"]
+    for q, code in zip(case["q"], case["code"]):
+        assert O.e2m1_rne_index(q) == code, q
+
+
+def test_e2m1_rne_bruteforce():
+    qs = np.concatenate([np.linspace(0, 8, 3201), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]])
+    prev = 0
+    for q in sorted(qs):
+        want = 7 if q >= 6 else nearest_even(Fraction(float(q)), E2M1_POS_FR)
+        got = O.e2m1_rne_index(q)
+        assert got == want, q
+        assert got >= prev
+        prev = got
+
+
+def test_e4m3_rne_hand(golden):
+    case = golden["e4m3_rne"]
+    for v, b in zip(case["v"], case["byte"]):
+        assert O.e4m3_rne(v) == b, v
+
+
+def test_e4m3_rne_matches_torch_cast():
+    pos = E4M3_ALL[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2           # exact ties, representable in fp32
+    rng = np.random.default_rng(7)
+    rand = np.exp(rng.uniform(np.log(2.0 ** -11), np.log(448.0), 4000))
+    vals = np.concatenate([pos, mids, rand]).astype(np.float32)
+    want = torch.tensor(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.e4m3_rne(float(v)) for v in vals])
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_rne_exact_rational():
+    rng = np.random.default_rng(8)
+    for v in np.exp(rng.uniform(np.log(2.0 ** -12), np.log(500.0), 500)):
+        want = 0x7E if v >= 448 else nearest_even(Fraction(float(v)), E4M3_POS_FR)
+        assert O.e4m3_rne(float(v)) == want
+
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(9)
+    f = (rng.standard_normal(20000) * np.exp(rng.uniform(-60, 60, 20000))).astype(np.float32)
+    # exact ties between neighbouring bf16 values
+    base = inputs.f32_to_bf16_bits(f[:1000]).astype(np.uint32) << 16
+    ties = (base | 0x8000).view(np.float32)
+    vals = np.concatenate([f, ties, np.float32([0.0, -0.0, 1.0, -3.5])])
+    want = torch.tensor(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.bf16_rne(vals.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rne_fp64_inputs():
+    cases = [
+        (1.0 + 2.0 ** -8, 0x3F80),                    # tie -> even (1.0)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),                # tie -> even (1 + 2^-6)
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),       # just above the tie: bits beyond fp32
+        (-(1.0 + 2.0 ** -8 + 2.0 ** -40), 0xBF81),
+        (2.0 ** -134, 0x0000),                         # subnormal tie 0 | 2^-133 -> 0
+        (3 * 2.0 ** -134, 0x0002),                     # tie 2^-133 | 2^-132 -> even
+        (float.fromhex("0x1.FFp127"), 0x7F80),         # tie max-finite | 2^128 -> inf
+        (float.fromhex("0x1.FEp127"), 0x7F7F),
+        (1e300, 0x7F80),
+    ]
+    for v, want in cases:
+        assert int(O.bf16_rne(v)) == want, (v, hex(int(O.bf16_rne(v))))
+
+
+def test_ulp_and_tolerance():
+    assert O.ulp_bf16(1.0) == 2.0 ** -7
+    assert O.ulp_bf16(1.99) == 2.0 ** -7
+    assert O.ulp_bf16(2.0) == 2.0 ** -6
+    assert O.ulp_bf16(-0.75) == 2.0 ** -8
+    assert O.ulp_bf16(0.0) == 2.0 ** -133
+    assert O.ulp_bf16(2.0 ** -140) == 2.0 ** -133
+    assert O.tolerance(np.array([1.0]), np.array([1000.0]))[0] == 1.0 + 2.0 ** -7
+
+
+# ---------------------------------------------------------------------------
+# quantiser (input recipe)
+
+
+def test_quantize_ties_block(golden):
+    c = golden["quantize_ties_block"]
+    W = np.array([c["row0"], c["row1"]], dtype=np.float32)
+    codes, scales, g = O.quantize(W)
+    assert g == c["gscale"]
+    assert scales[0, 0] == c["row0_scale"] and scales[1, 0] == c["row1_scale"]
+    got = np.empty(16, dtype=np.int64)
+    got[0::2], got[1::2] = codes[0] & 15, codes[0] >> 4
+    assert got.tolist() == c["row0_codes"]
+
+
+def test_quantize_matches_exact_rational():
+    rng = np.random.default_rng(11)
+    W = inputs.weights_f32(6, 64, seed=5)
+    W = inputs.add_zero_and_outlier_blocks(W, seed=6, frac_zero=0.1, frac_outlier=0.1)
+    # crafted exact ties: tensor scale 1 (amax 2688), block amax 102 -> 17 = 16|18 tie
+    T = np.zeros((3, 32), dtype=np.float32)
+    T[0, 0] = 2688.0
+    T[1, :16] = np.float32([102, -40, 8, 24, 40, 56, 4, 12, 20, 28, 36, 44, 52, 60, 80, -0.0])
+    T[2, 16:] = np.float32(rng.standard_normal(16) * 1e-4)   # sub-normal-scale block
+    T[2, 3] = -0.0
+    for M in (W, T, inputs.weights_f32(3, 32, seed=12) * np.float32(1e-30)):
+        assert [a.tolist() if hasattr(a, "tolist") else a for a in O.quantize(M)] == \
+               [a.tolist() if hasattr(a, "tolist") else a for a in exact_quantize(M)]
+
+
+def test_quantize_all_zero_and_signed_zero():
+    codes, scales, g = O.quantize(np.zeros((2, 32), dtype=np.float32))
+    assert g == 0.0 and not scales.any() and not codes.any()
+    W = np.zeros((1, 16), dtype=np.float32)
+    W[0, 0], W[0, 1], W[0, 2] = 1.0, -0.0, -1e-6
+    codes, _, _ = O.quantize(W)
+    assert codes[0, 0] >> 4 == 8          # -0.0 keeps its sign bit
+    assert codes[0, 1] & 15 == 8          # a tiny negative rounds to -0
+
+
+def test_quantize_reconstruction_bound():
+    W = inputs.weights_f32(64, 256, seed=13)
+    codes, scales, g = O.quantize(W)
+    deq = O.dequant(codes, scales, g)
+    d = np.repeat(np.array([[O.e4m3(s) for s in row] for row in scales]), 16, axis=1) * g
+    # every element lies within half the widest E2M1 grid gap (2 at [4, 6]) of its code,
+    # plus the overshoot allowed when the block scale rounded down (amax/d <= 6.4)
+    assert np.all(np.abs(W - deq) <= 1.0 * d + 0.4 * d)
+    amax_b = np.abs(W.reshape(64, 16, 16)).max(axis=2)
+    ratio = amax_b / (d[:, ::16])
+    assert np.all((ratio > 5.6) & (ratio < 6.4))
+
+
+# ---------------------------------------------------------------------------
+# dequant and GEMV
+
+
+def test_dequant_matches_independent_decode():
+    rng = np.random.default_rng(14)
+    codes, scales = random_packed(rng, 7, 96)
+    g = 0.37
+    assert np.array_equal(O.dequant(codes, scales, g), decode_dense_independent(codes, scales, g))
+
+
+def test_gemv_hand_blocks(golden):
+    for case in golden["gemv"]:
+        K = case["K"]
+        codes = np.array([case["codes_bytes"]], dtype=np.uint8)
+        scales = np.array([case["scales"]], dtype=np.uint8)
+        X = inputs.f32_to_bf16_bits(np.array([case["x"]], dtype=np.float32))
+        assert codes.shape[1] * 2 == K
+        Y, A = O.gemv(codes, scales, case["gscale"], X)
+        assert Y[0, 0] == case["y"], case["id"]
+        y1, _ = O.gemv_one(codes, scales, case["gscale"], X, 0, 0)
+        assert y1 == case["y"]
+
+
+@pytest.mark.parametrize("N,K,n", [(5, 48, 3), (33, 160, 16), (64, 16, 1)])
+def test_gemv_matches_numpy_matmul(N, K, n):
+    rng = np.random.default_rng(N * 1000 + K)
+    codes, scales = random_packed(rng, N, K, scale_max=0x50)
+    g = float(np.float32(0.013))
+    X = inputs.activations_bf16(n, K, seed=N + K)
+    Wd = decode_dense_independent(codes, scales, g)
+    Xd = inputs.bf16_bits_to_f32(X).astype(np.float64)
+    Y, A = O.gemv(codes, scales, g, X)
+    assert Y.shape == (n, N)
+    assert np.all(np.abs(Y - Xd @ Wd.T) <= 1e-12 * (np.abs(Xd) @ np.abs(Wd).T) + 1e-300)
+    assert np.allclose(A, np.abs(Xd) @ np.abs(Wd).T, rtol=1e-12, atol=0)
+
+
+def test_gemv_exact_rational_bruteforce():
+    rng = np.random.default_rng(15)
+    N, K, n = 4, 48, 3
+    codes, scales = random_packed(rng, N, K, scale_max=0x60)
+    g = float(np.float32(0.0123))
+    X = inputs.activations_bf16(n, K, seed=16)
+    Y, A = O.gemv(codes, scales, g, X)
+    xs = inputs.bf16_bits_to_f32(X)
+    for t in range(n):
+        for r in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                byte = int(codes[r, k // 2])
+                c = byte & 15 if k % 2 == 0 else byte >> 4
+                acc += e2m1_from_fields(c) * E4M3_POS_FR[int(scales[r, k // 16])] * \
+                    Fraction(g) * Fraction(float(xs[t, k]))
+            assert abs(Fraction(Y[t, r]) - acc) <= Fraction(K) * Fraction(2) ** -52 * Fraction(A[t, r])
+
+
+def test_gemv_invariants():
+    rng = np.random.default_rng(17)
+    N, K, n = 24, 128, 5
+    codes, scales = random_packed(rng, N, K, scale_max=0x58)
+    g = 0.021
+    X = inputs.activations_bf16(n, K, seed=18)
+    Y, A = O.gemv(codes, scales, g, X)
+    Yneg, _ = O.gemv(codes, scales, g, X ^ np.uint16(0x8000))     # -x
+    assert np.array_equal(Yneg, -Y)
+    X4 = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(X) * np.float32(4))
+    Y4, A4 = O.gemv(codes, scales, g, X4)
+    assert np.array_equal(Y4, 4 * Y) and np.array_equal(A4, 4 * A)
+    perm = np.array([3, 0, 4, 1, 2])
+    Yp, _ = O.gemv(codes, scales, g, X[perm])
+    assert np.array_equal(Yp, Y[perm])
+    Yz, Az = O.gemv(np.zeros_like(codes), scales, g, X)
+    assert not Yz.any() and not Az.any()
+
+
+def test_gemv_one_matches_gemv():
+    rng = np.random.default_rng(19)
+    codes, scales = random_packed(rng, 9, 64)
+    X = inputs.activations_bf16(4, 64, seed=20)
+    Y, A = O.gemv(codes, scales, 0.5, X)
+    for t, r in [(0, 0), (3, 8), (2, 5)]:
+        y, a = O.gemv_one(codes, scales, 0.5, X, t, r)
+        assert y == Y[t, r] and a == A[t, r]
+
+
+def test_qkv_scatter():
+    Y = np.arange(2 * 4, dtype=np.float64).reshape(2, 4)
+    out = O.qkv_scatter(Y, (2, 1, 1), (0, 3, 5), ldy=7, fill=-1.0)
+    assert out.tolist() == [[0, 1, -1, 2, -1, 3, -1], [4, 5, -1, 6, -1, 7, -1]]
