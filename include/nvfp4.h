@@ -1,0 +1,150 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4, the MI355X (gfx950) NVFP4 weight-only
+ * projection GEMV of batched LLM decode.
+ *
+ * The operation (Atlas PR #266, PR description "What it does"): for n
+ * concurrent decode tokens, one projection computes
+ *
+ *     Y[t][r] = gscale * sum_k X[t][k] * e2m1(code[r][k]) * e4m3(scale[r][k/16])
+ *
+ * for t < n, r < N, reading the NVFP4 weight matrix once for all n tokens
+ * instead of once per token (the tiling section of the same page: "each tile
+ * reads the q/k/v/o projection weights ONCE for its tokens").  The page's
+ * greedy 3-token tiling is available as an explicit schedule
+ * (nvfp4_gemv_sched); the default launch reads the weights once for n <= 16.
+ *
+ * Number formats: the pages name NVFP4 without defining its bits.  Codes are
+ * OCP FP4 E2M1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}), block scales OCP
+ * FP8 E4M3FN (bias 7, max 448, 0x7F/0xFF NaN), one scale per 16 consecutive k
+ * of a row, and one fp32 tensor multiplier gscale.  X and Y are bf16 bit
+ * patterns, accumulation is fp32, Y is rounded to nearest even.
+ *
+ * Conventions for every entry point:
+ *   - all array pointers are DEVICE pointers; calls are asynchronous on
+ *     `stream` (a hipStream_t; NULL is the default stream);
+ *   - the caller allocates and owns every buffer; the GEMV entry points
+ *     allocate nothing, cache no pointer and never synchronise;
+ *   - arguments are validated on the host before any HIP call; a failed
+ *     validation returns a status and launches nothing;
+ *   - no exception crosses the ABI; nvfp4_strerror names every status.
+ *
+ * Layouts:
+ *   canonical codes  [N][K/2] u8: element (r,k) in byte r*K/2 + k/2, low
+ *                    nibble for even k, high nibble for odd k;
+ *   canonical scales [N][K/16] u8: one E4M3 byte per 16 consecutive k;
+ *   packed (device)  layout written by nvfp4_pack and read by the GEMV
+ *                    entry points: rows padded to a multiple of 16 and K to
+ *                    a multiple of 128 with zero codes, stored as 16-row x
+ *                    128-column tiles whose 1 KiB of codes is one 16-byte
+ *                    load per lane of a 64-lane wavefront; its byte sizes
+ *                    are nvfp4_packed_codes_bytes / nvfp4_packed_scales_bytes;
+ *   X [n][K] bf16 row-major (token-major), Y [n][N] bf16 row-major.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    NVFP4_ERR_RANGE = 2,     /* n outside [1,16], N or K not positive, bad rows */
+    NVFP4_ERR_ALIGN = 3,     /* a pointer is not aligned as documented          */
+    NVFP4_ERR_SHAPE = 4,     /* K not a multiple of 16, or a size limit         */
+    NVFP4_ERR_SCHEDULE = 5,  /* an explicit tile schedule is invalid            */
+    NVFP4_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch               */
+    NVFP4_ERR_DEVICE = 7     /* the current device is not a gfx950 GPU          */
+} nvfp4_status;
+
+/* Largest number of tokens one launch covers (the decode batch of the pages:
+ * up to 16 concurrent sequences, Atlas PR #266 A/B table, C = 1..16). */
+#define NVFP4_MAX_TOKENS 16
+
+/* Byte sizes of the packed device layout for an N x K weight.  0 if N <= 0
+ * or K <= 0 or K % 16 != 0. */
+size_t nvfp4_packed_codes_bytes(int N, int K);
+size_t nvfp4_packed_scales_bytes(int N, int K);
+
+/* Quantise an fp32 weight W [N][K] (device, row-major, finite values) to the
+ * canonical NVFP4 layout with the recipe: gscale = fp32(amax / (6*448));
+ * per 16-block scale = E4M3 round-to-nearest-even of amax_block/(6*gscale),
+ * saturating at 448; code = sign(w) | E2M1 round-to-nearest-even of
+ * |w| / (scale*gscale) (magnitude 0 when that product is 0).
+ * tensor_scale: device float[2]; [0] receives gscale, [1] the tensor amax.
+ * codes: [N][K/2], scales: [N][K/16] (canonical).  Requires K % 16 == 0,
+ * W 16-byte aligned.  Errors: NULL, RANGE, SHAPE, ALIGN, LAUNCH. */
+int nvfp4_quantize(const float *W, int N, int K, uint8_t *codes, uint8_t *scales,
+                   float *tensor_scale, void *stream);
+
+/* Reorder canonical codes/scales (device) into the packed device layout
+ * (device buffers of nvfp4_packed_*_bytes; the padding is written as zeros).
+ * One-time, at weight load.  Errors: NULL, RANGE, SHAPE, ALIGN (packed
+ * buffers must be 16-byte aligned), LAUNCH. */
+int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K,
+               uint8_t *codes_packed, uint8_t *scales_packed, void *stream);
+
+/* Y[n][N] = X[n][K] . dequant(W)^T for 1 <= n <= 16 tokens.
+ * Wq / Wscale: packed layout (nvfp4_pack), 16-byte aligned.
+ * X: bf16 [n][K], 8-byte aligned.  Y: bf16 [n][N], 2-byte aligned.
+ * Each token's result is bit-identical to the same token computed alone
+ * (n = 1) and under any schedule of nvfp4_gemv_sched.
+ * Errors: NULL, RANGE, SHAPE (K % 16), ALIGN, LAUNCH, DEVICE. */
+int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+               const uint16_t *X, uint16_t *Y, int n, int N, int K, void *stream);
+
+/* Fused QKV projection (Atlas PR #266, PR description, multi_seq/qkv.rs
+ * bullet: one fused weight whose q, k and v rows land at fixed offsets of a
+ * per-sequence buffer).  W has N = rows[0]+rows[1]+rows[2] rows: rows
+ * [0,rows[0]) are q, the next rows[1] are k, the last rows[2] are v.  Token t's
+ * q/k/v outputs are written straight to Y + t*ldy + out_off[p] + j (j < rows[p])
+ * with no scratch buffer and no device-to-device copy.  The three output
+ * ranges must not overlap and must fit in ldy (ldy >= out_off[p] + rows[p]).
+ * rows / out_off are HOST arrays read during the call.  Same bit-identity
+ * guarantees as nvfp4_gemv; results equal the three slices of nvfp4_gemv on
+ * the same weight bit for bit.  Errors: as nvfp4_gemv, RANGE for bad
+ * rows/out_off/ldy. */
+int nvfp4_gemv_qkv(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+                   const uint16_t *X, uint16_t *Y, int n, int K,
+                   const int32_t rows[3], const int64_t out_off[3], int64_t ldy,
+                   void *stream);
+
+/* nvfp4_gemv under an explicit token-tile schedule: tile_widths (HOST array
+ * of ntiles entries, each in [1,16], summing to n) splits the n tokens into
+ * consecutive tiles, each one launch that reads the whole weight once.  This
+ * is how the pages' greedy [3,3,...,2|1] tiling (Atlas PR #266 description)
+ * is reproduced for comparison.  Errors: as nvfp4_gemv, SCHEDULE for a bad
+ * schedule (never a silent fallback). */
+int nvfp4_gemv_sched(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+                     const uint16_t *X, uint16_t *Y, int n, int N, int K,
+                     const uint8_t *tile_widths, int ntiles, void *stream);
+
+/* The dispatcher's schedule for (n, N, K): writes the tile widths nvfp4_gemv
+ * uses into widths (HOST, capacity max_tiles) and returns their count, or a
+ * negative status.  Pure host function. */
+int nvfp4_schedule(int n, int N, int K, uint8_t *widths, int max_tiles);
+
+/* The pages' greedy schedule: tiles of `width` tokens, then one remainder
+ * tile (Atlas PR #266 description: "greedy 3s, then a 2-or-1 remainder"; n=8
+ * costs 3 weight reads).  Returns the tile count or a negative status.  Pure
+ * host function. */
+int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles);
+
+/* Launch geometry the library uses for (n, N, K): workgroups, waves per
+ * workgroup and 128-column tiles per wave.  Pure host function; returns a
+ * status. */
+int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves,
+                          int *tiles_per_wave);
+
+/* Human-readable name of a status code (static storage). */
+const char *nvfp4_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,783 @@
+// libnvfp4: NVFP4 weight-only projection GEMV of batched LLM decode on MI355X
+// (gfx950), behind the C ABI of include/nvfp4.h.
+//
+// What is computed (Atlas PR #266, PR description "What it does"): for n <= 16
+// concurrent decode tokens, Y[t][r] = gscale * sum_k X[t][k] * w(r,k) with w an
+// NVFP4 weight (E2M1 code times the E4M3 scale of its 16-element K-block), the
+// weight matrix read once for all tokens.
+//
+// Design (gfx950-first; the pages' CUDA kernels are prior art only):
+//  * Packed layout: 16-row x 128-column tiles.  A tile's 1 KiB of codes is one
+//    16-byte load per lane of a 64-lane wavefront, laid out so that the bytes a
+//    lane loads are exactly the MFMA operand fragments it feeds; the tile's 128
+//    scale bytes are one 8-byte load per row.
+//  * Dequant in registers: v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 codes into
+//    two exact bf16 values per instruction.  The E4M3 block scale is NOT folded
+//    into that conversion (the hardware applies only the exponent of its f32
+//    scale operand); instead each 16-element K-block is one
+//    v_mfma_f32_16x16x16_bf16 whose fp32 partial is multiplied by the block
+//    scale with one fp32 FMA per output.
+//  * Tokens are the MFMA M dimension, padded to 16: every n runs the identical
+//    instruction sequence, so a token's result never depends on n or on the
+//    other tokens of the launch (bit-identity with the n = 1 result).
+//  * Persistent workgroups: each wave owns a fixed K-slice; its slice of X sits
+//    in VGPRs for the whole launch (loaded once, straight in MFMA A-operand
+//    layout), and it streams the weight tiles of its slice for consecutive
+//    16-row groups, prefetching the next row group's tiles while it computes
+//    the current one, so loads stay in flight across the dequant work.
+//  * K-slice partials are summed through LDS in a fixed wave order, then
+//    scaled by gscale and rounded to bf16 (RNE) in the epilogue, which writes
+//    each projection's rows straight to its output offset (fused QKV).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <type_traits>
+
+#include "../../include/nvfp4.h"
+
+namespace {
+
+typedef unsigned int u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowsPerGroup = 16;      // MFMA N dimension: weight rows per tile
+constexpr int kTileK = 128;            // K columns per tile (8 NVFP4 blocks)
+constexpr int kBlocksPerTile = kTileK / 16;
+constexpr int kMaxTilesPerWave = 8;    // X slice of a wave: 16 VGPRs per tile
+constexpr int kMaxWaves = 8;
+
+struct GemvParams {
+    const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
+    const u32x2 *scales;   // packed scales, [RG][T][16 rows] x 8 B
+    const uint16_t *X;     // bf16 [n][K]
+    uint16_t *Y;           // bf16 output, token stride ldy
+    float gscale;
+    int n, N, K, T, RG;
+    int start1, start2;    // first row of the 2nd and 3rd projection (N if absent)
+    long long off0, off1, off2, ldy;
+};
+
+// Two E2M1 codes (byte `sel` of w) -> two bf16 values, unscaled (scale 1.0).
+__device__ __forceinline__ u32 fp4x2_to_bf16x2(u32 w, int sel)
+{
+    bf16x2 v;
+    switch (sel) {
+    case 0: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0); break;
+    case 1: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1); break;
+    case 2: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2); break;
+    default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3); break;
+    }
+    return __builtin_bit_cast(u32, v);
+}
+
+// E4M3FN byte `sel` of w -> f32 (exact; gfx950 decodes the OCP encoding).
+__device__ __forceinline__ float fp8_to_f32(u32 w, int sel)
+{
+    switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+    }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: RNE
+}
+
+// One launch covers every token (n <= 16) of one weight matrix.
+//   W  waves per workgroup, each owning a contiguous K-slice of MT tiles;
+//   EXACT: every wave owns exactly MT tiles (T == W * MT), no predication.
+template <int W, int MT, bool EXACT>
+__global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i = lane & 15;   // token row of A, weight row of B and C
+    const int g = lane >> 4;   // K quarter of A and B, token quarter of C
+
+    const int rg0 = (int)(((unsigned long long)blockIdx.x * (unsigned)p.RG) / gridDim.x);
+    const int rg1 = (int)(((unsigned long long)(blockIdx.x + 1) * (unsigned)p.RG) / gridDim.x);
+    const int tw0 = wave * MT;
+    const int tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+
+    // This wave's K-slice of X, in MFMA A-operand layout: lane (i, g) holds
+    // X[i][k .. k+3] with k = 16*block + 4*g, for every block of the slice.
+    // Lanes of tokens >= n load token 0's values and zero them.  When the
+    // slices tile K exactly (EXACT, K == 128*T) no column check is needed and
+    // all loads share one base address with immediate offsets.
+    u32x2 xr[MT][kBlocksPerTile];
+    const bool tok_ok = i < p.n;
+    const uint16_t *xrow = p.X + (size_t)(tok_ok ? i : 0) * p.K + 4 * g;
+    if constexpr (EXACT) {
+        const u32x2 *xp = reinterpret_cast<const u32x2 *>(xrow + tw0 * kTileK);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int b = 0; b < kBlocksPerTile; ++b)
+                xr[t][b] = xp[(t * kTileK + b * 16) / 4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int b = 0; b < kBlocksPerTile; ++b)
+                xr[t][b] = tok_ok ? xr[t][b] : u32x2{0u, 0u};
+    } else {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+            for (int b = 0; b < kBlocksPerTile; ++b) {
+                const int k = ((tw0 + t) * kBlocksPerTile + b) * 16;
+                const bool ok = tok_ok && t < tw && k + 4 * g < p.K;
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(xrow + (ok ? k : 0));
+                xr[t][b] = ok ? v : u32x2{0u, 0u};
+            }
+        }
+    }
+
+    // Weight tiles in flight: slot t holds tile t of the current row group's
+    // slice until it is consumed, then the same tile of the next row group.
+    // Every workgroup owns at least one row group (the host launches at most
+    // RG workgroups), so the first tiles are loaded unconditionally, in slot
+    // order, as the loop body reloads them.
+    u32x4 wc[MT];
+    u32x2 ws[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        wc[t] = u32x4{0u, 0u, 0u, 0u};
+        ws[t] = u32x2{0u, 0u};
+        if (EXACT || t < tw) {
+            const size_t tile = (size_t)rg0 * p.T + tw0 + t;
+            wc[t] = __builtin_nontemporal_load(p.codes + tile * 64 + lane);
+            ws[t] = __builtin_nontemporal_load(p.scales + tile * 16 + i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    __shared__ f32x4 part[2][W][64];
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // One row group of this wave's K-slice.  PF: refill each ring slot with
+    // the next row group's tile as soon as the slot is read.  Blocks run as a
+    // software pipeline (the scale FMA of a block trails its MFMA by two
+    // blocks); scheduling barriers keep the compiler from hoisting all MFMAs
+    // ahead of their FMAs, which would hold every partial in registers.
+    auto rowgroup = [&](auto pf_tag, int rg) -> f32x4 {
+        constexpr bool PF = decltype(pf_tag)::value;
+        f32x4 acc = zero, p1 = zero, p2 = zero;
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (EXACT || t < tw) {
+                const u32x4 c = wc[t];
+                const u32x2 s = ws[t];
+#pragma unroll
+                for (int b = 0; b < kBlocksPerTile; ++b) {
+                    // B operand: W[row i][16*block + 4*g + e], e = 0..3, from
+                    // bytes 2*(b&1) and 2*(b&1)+1 of dword b/2.
+                    const u32 cw = c[b >> 1];
+                    const u32 lo = fp4x2_to_bf16x2(cw, (b & 1) * 2);
+                    const u32 hi = fp4x2_to_bf16x2(cw, (b & 1) * 2 + 1);
+                    const s16x4 bop = __builtin_bit_cast(s16x4, u32x2{lo, hi});
+                    const s16x4 aop = __builtin_bit_cast(s16x4, xr[t][b]);
+                    const f32x4 pr = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, zero, 0, 0, 0);
+                    const float sc = fp8_to_f32(s[b >> 2], b & 3);
+                    acc[0] = __builtin_fmaf(s2, p2[0], acc[0]);
+                    acc[1] = __builtin_fmaf(s2, p2[1], acc[1]);
+                    acc[2] = __builtin_fmaf(s2, p2[2], acc[2]);
+                    acc[3] = __builtin_fmaf(s2, p2[3], acc[3]);
+                    p2 = p1;
+                    s2 = s1;
+                    p1 = pr;
+                    s1 = sc;
+                    // Pin the FMAs of this step here (instruction selection
+                    // would otherwise sink the whole FMA chain below every
+                    // MFMA and keep all partials live).
+                    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+                }
+                // Refill the slot once its codes and scales are consumed, so
+                // the next tile lands in the same registers (no copy, and no
+                // wait on the other slots at the top of the next row group).
+                if constexpr (PF) {
+                    const size_t tile = (size_t)(rg + 1) * p.T + tw0 + t;
+                    wc[t] = __builtin_nontemporal_load(p.codes + tile * 64 + lane);
+                    ws[t] = __builtin_nontemporal_load(p.scales + tile * 16 + i);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[v] = __builtin_fmaf(s1, p1[v], __builtin_fmaf(s2, p2[v], acc[v]));
+        return acc;
+    };
+
+    // Sum the K-slices of row group rg in wave order 0..W-1 and store it.
+    auto finish = [&](int rg, const f32x4 acc) {
+        part[rg & 1][wave][lane] = acc;
+        __syncthreads();
+        if (wave == (rg - rg0) % W) {
+            f32x4 sum = part[rg & 1][0][lane];
+#pragma unroll
+            for (int w = 1; w < W; ++w) {
+                const f32x4 q = part[rg & 1][w][lane];
+                sum[0] = sum[0] + q[0];
+                sum[1] = sum[1] + q[1];
+                sum[2] = sum[2] + q[2];
+                sum[3] = sum[3] + q[3];
+            }
+            const int r = rg * kRowsPerGroup + i;
+            if (r < p.N) {
+                long long off;
+                if (r >= p.start2)
+                    off = p.off2 + (r - p.start2);
+                else if (r >= p.start1)
+                    off = p.off1 + (r - p.start1);
+                else
+                    off = p.off0 + r;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int tok = 4 * g + v;
+                    if (tok < p.n)
+                        p.Y[(long long)tok * p.ldy + off] = f32_to_bf16_bits(p.gscale * sum[v]);
+                }
+            }
+        }
+    };
+
+    // Every row group but the last prefetches its successor; the last one is
+    // peeled so both loop bodies are straight-line code.
+    int rg = rg0;
+    for (; rg + 1 < rg1; ++rg)
+        finish(rg, rowgroup(std::true_type{}, rg));
+    if (rg < rg1)
+        finish(rg, rowgroup(std::false_type{}, rg));
+}
+
+// ---- pack: canonical -> tiled device layout --------------------------------
+
+// One thread per 16-byte lane chunk of a tile.
+__global__ void nvfp4_pack_codes_kernel(const uint8_t *codes, int N, int K, int T, long long chunks,
+                                        u32x4 *out)
+{
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= chunks)
+        return;
+    const int l = (int)(idx & 63);
+    const long long tile_lin = idx >> 6;
+    const int tile = (int)(tile_lin % T);
+    const long long rg = tile_lin / T;
+    const int i = l & 15, g = l >> 4;
+    const long long row = rg * kRowsPerGroup + i;
+    u32 w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        // packed byte q holds K = tile*128 + 16*(q/2) + 4*g + 2*(q%2) (+0, +1)
+        const int k = tile * kTileK + 16 * (q >> 1) + 4 * g + 2 * (q & 1);
+        u32 byte = 0;
+        if (row < N && k < K)
+            byte = codes[row * (long long)(K / 2) + k / 2];
+        w[q >> 2] |= byte << (8 * (q & 3));
+    }
+    out[idx] = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// One thread per (row group, tile, row): the 8 scale bytes of that row's tile.
+__global__ void nvfp4_pack_scales_kernel(const uint8_t *scales, int N, int K, int T, long long items,
+                                         u32x2 *out)
+{
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= items)
+        return;
+    const int i = (int)(idx & 15);
+    const long long tile_lin = idx >> 4;
+    const int tile = (int)(tile_lin % T);
+    const long long rg = tile_lin / T;
+    const long long row = rg * kRowsPerGroup + i;
+    const int nb = K / 16;
+    u32 w[2] = {0u, 0u};
+#pragma unroll
+    for (int b = 0; b < kBlocksPerTile; ++b) {
+        const int blk = tile * kBlocksPerTile + b;
+        u32 byte = 0;
+        if (row < N && blk < nb)
+            byte = scales[row * (long long)nb + blk];
+        w[b >> 2] |= byte << (8 * (b & 3));
+    }
+    out[idx] = u32x2{w[0], w[1]};
+}
+
+// ---- quantise (input recipe) --------------------------------------------------
+
+__global__ void nvfp4_amax_init_kernel(float *ts)
+{
+    ts[1] = 0.0f;
+}
+
+__global__ void nvfp4_amax_kernel(const float4 *W, long long n4, float *ts)
+{
+    float m = 0.0f;
+    for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < n4;
+         j += (long long)gridDim.x * blockDim.x) {
+        const float4 v = W[j];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    for (int o = 32; o > 0; o >>= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0)   // non-negative floats order like their bit patterns
+        atomicMax(reinterpret_cast<unsigned int *>(ts + 1), __float_as_uint(m));
+}
+
+// E4M3FN byte (0x00..0x7E) -> exact value, from its fields.
+__device__ __forceinline__ double e4m3_value(int s)
+{
+    const int e = (s >> 3) & 15, m = s & 7;
+    return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+// Nearest E4M3FN byte for v >= 0, ties to even, saturating at 448.
+__device__ __forceinline__ int e4m3_rne(double v)
+{
+    if (!(v < 448.0))
+        return 0x7E;
+    if (v < 0.015625)   // below 2^-6: subnormal grid of step 2^-9
+        return (int)rint(v * 512.0);
+    int e;
+    const double f = frexp(v, &e);   // v = f * 2^e, f in [0.5, 1)
+    int E = e + 6;
+    int M = (int)rint((f * 2.0 - 1.0) * 8.0);
+    if (M == 8) {
+        E += 1;
+        M = 0;
+    }
+    const int byte = (E << 3) | M;
+    return byte > 0x7E ? 0x7E : byte;
+}
+
+// E2M1 magnitude index of a / d (a >= 0, d > 0), nearest with ties to the even
+// index, by exact comparisons against the midpoints of the grid.
+__device__ __forceinline__ int e2m1_rne(double a, double d)
+{
+    int idx = 0;
+    idx += a > 0.25 * d;
+    idx += a >= 0.75 * d;
+    idx += a > 1.25 * d;
+    idx += a >= 1.75 * d;
+    idx += a > 2.5 * d;
+    idx += a >= 3.5 * d;
+    idx += a > 5.0 * d;
+    return idx;
+}
+
+// One thread per 16-element K-block (flat index row*(K/16) + block).
+__global__ void nvfp4_quantize_kernel(const float4 *W, long long nblocks, uint2 *codes,
+                                      uint8_t *scales, float *ts)
+{
+    const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const float amax = ts[1];
+    const float gs = (float)((double)amax / 2688.0);
+    if (blk == 0)
+        ts[0] = gs;
+    if (blk >= nblocks)
+        return;
+    float w[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float4 v = W[blk * 4 + j];
+        w[4 * j] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
+    }
+    double am = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        am = fmax(am, fabs((double)w[j]));
+    const int s = gs > 0.0f ? e4m3_rne(am / (6.0 * (double)gs)) : 0;
+    const double d = e4m3_value(s) * (double)gs;
+    u32 c[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int mag = d > 0.0 ? e2m1_rne(fabs((double)w[j]), d) : 0;
+        const u32 code = (u32)mag | (signbit(w[j]) ? 8u : 0u);
+        c[j >> 3] |= code << (4 * (j & 7));
+    }
+    codes[blk] = make_uint2(c[0], c[1]);
+    scales[blk] = (uint8_t)s;
+}
+
+// ---- host side ---------------------------------------------------------------
+
+typedef void (*GemvKernel)(GemvParams);
+
+template <int W, int MT>
+GemvKernel pick_exact(bool exact)
+{
+    return exact ? nvfp4_gemv_kernel<W, MT, true> : nvfp4_gemv_kernel<W, MT, false>;
+}
+
+template <int W>
+GemvKernel pick_mt(int mt, bool exact)
+{
+    switch (mt) {
+    case 1: return pick_exact<W, 1>(exact);
+    case 2: return pick_exact<W, 2>(exact);
+    case 3: return pick_exact<W, 3>(exact);
+    case 4: return pick_exact<W, 4>(exact);
+    case 5: return pick_exact<W, 5>(exact);
+    case 6: return pick_exact<W, 6>(exact);
+    case 7: return pick_exact<W, 7>(exact);
+    default: return pick_exact<W, 8>(exact);
+    }
+}
+
+GemvKernel pick_kernel(int waves, int mt, bool exact)
+{
+    switch (waves) {
+    case 1: return pick_mt<1>(mt, exact);
+    case 2: return pick_mt<2>(mt, exact);
+    case 4: return pick_mt<4>(mt, exact);
+    default: return pick_mt<8>(mt, exact);
+    }
+}
+
+struct Geometry {
+    int workgroups, waves, mt;
+    bool exact;
+};
+
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+int g_is_gfx950[kMaxDevices];   // 0 unknown, 1 yes, -1 no
+std::mutex g_dev_mutex;
+
+// Compute units and architecture of the current device, looked up once.
+int current_device_info(int *cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return NVFP4_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_is_gfx950[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return NVFP4_ERR_DEVICE;
+        g_is_gfx950[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_cus[dev] = prop.multiProcessorCount;
+    }
+    if (g_is_gfx950[dev] != 1)
+        return NVFP4_ERR_DEVICE;
+    *cus = g_cus[dev];
+    return NVFP4_OK;
+}
+
+bool geometry_for(int N, int K, int cus, Geometry *geo)
+{
+    const int T = (K + kTileK - 1) / kTileK;
+    const int RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    geo->exact = false;
+    geo->waves = 0;
+    for (int w = kMaxWaves; w >= 1 && K % kTileK == 0; w >>= 1) {
+        if (T % w == 0 && T / w <= kMaxTilesPerWave) {
+            geo->waves = w;
+            geo->mt = T / w;
+            geo->exact = true;
+            break;
+        }
+    }
+    if (!geo->exact) {
+        if ((T + kMaxWaves - 1) / kMaxWaves > kMaxTilesPerWave)
+            return false;
+        geo->waves = kMaxWaves;
+        geo->mt = (T + kMaxWaves - 1) / kMaxWaves;
+    }
+    const int per_cu = geo->waves >= 8 ? 1 : 8 / geo->waves;
+    long long wg = (long long)cus * per_cu;
+    geo->workgroups = (int)(RG < wg ? RG : wg);
+    return true;
+}
+
+bool aligned(const void *p, size_t a)
+{
+    return ((uintptr_t)p % a) == 0;
+}
+
+int validate_common(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X, const uint16_t *Y,
+                    int n, int N, int K)
+{
+    if (!Wq || !Wscale || !X || !Y)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    const int T = (K + kTileK - 1) / kTileK;
+    if ((T + kMaxWaves - 1) / kMaxWaves > kMaxTilesPerWave)
+        return NVFP4_ERR_SHAPE;   // K > 8192: the X slice would not fit in VGPRs
+    if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 8) || !aligned(Y, 2))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+int launch_gemv(const GemvParams &p, hipStream_t stream)
+{
+    int cus = 0;
+    int st = current_device_info(&cus);
+    if (st != NVFP4_OK)
+        return st;
+    Geometry geo;
+    if (!geometry_for(p.N, p.K, cus, &geo))
+        return NVFP4_ERR_SHAPE;
+    GemvKernel k = pick_kernel(geo.waves, geo.mt, geo.exact);
+    hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(geo.waves * 64), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+GemvParams make_params(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
+                       uint16_t *Y, int n, int N, int K)
+{
+    GemvParams p;
+    p.codes = reinterpret_cast<const u32x4 *>(Wq);
+    p.scales = reinterpret_cast<const u32x2 *>(Wscale);
+    p.X = X;
+    p.Y = Y;
+    p.gscale = gscale;
+    p.n = n;
+    p.N = N;
+    p.K = K;
+    p.T = (K + kTileK - 1) / kTileK;
+    p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    p.start1 = N;
+    p.start2 = N;
+    p.off0 = p.off1 = p.off2 = 0;
+    p.ldy = N;
+    return p;
+}
+
+int check_schedule(int n, const uint8_t *tile_widths, int ntiles)
+{
+    if (!tile_widths || ntiles < 1 || ntiles > n)
+        return NVFP4_ERR_SCHEDULE;
+    int sum = 0;
+    for (int j = 0; j < ntiles; ++j) {
+        if (tile_widths[j] < 1 || tile_widths[j] > NVFP4_MAX_TOKENS)
+            return NVFP4_ERR_SCHEDULE;
+        sum += tile_widths[j];
+    }
+    return sum == n ? NVFP4_OK : NVFP4_ERR_SCHEDULE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_packed_codes_bytes(int N, int K)
+{
+    if (N <= 0 || K <= 0 || K % 16 != 0)
+        return 0;
+    const size_t RG = (size_t)(N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const size_t T = (size_t)(K + kTileK - 1) / kTileK;
+    return RG * T * 1024;
+}
+
+size_t nvfp4_packed_scales_bytes(int N, int K)
+{
+    if (N <= 0 || K <= 0 || K % 16 != 0)
+        return 0;
+    const size_t RG = (size_t)(N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const size_t T = (size_t)(K + kTileK - 1) / kTileK;
+    return RG * T * 128;
+}
+
+int nvfp4_quantize(const float *W, int N, int K, uint8_t *codes, uint8_t *scales,
+                   float *tensor_scale, void *stream)
+{
+    if (!W || !codes || !scales || !tensor_scale)
+        return NVFP4_ERR_NULL;
+    if (N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    int cus = 0;
+    int st = current_device_info(&cus);
+    if (st != NVFP4_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const long long nblocks = (long long)N * (K / 16);
+    hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+    const long long n4 = nblocks * 4;
+    long long grid = (n4 + 255) / 256;
+    if (grid > (long long)cus * 8)
+        grid = (long long)cus * 8;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(W), n4, tensor_scale);
+    hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(W), nblocks, reinterpret_cast<uint2 *>(codes),
+                       scales, tensor_scale);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K, uint8_t *codes_packed,
+               uint8_t *scales_packed, void *stream)
+{
+    if (!codes || !scales || !codes_packed || !scales_packed)
+        return NVFP4_ERR_NULL;
+    if (N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!aligned(codes_packed, 16) || !aligned(scales_packed, 16))
+        return NVFP4_ERR_ALIGN;
+    int cus = 0;
+    int st = current_device_info(&cus);
+    if (st != NVFP4_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int T = (K + kTileK - 1) / kTileK;
+    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const long long chunks = RG * T * 64;
+    const long long items = RG * T * 16;
+    hipLaunchKernelGGL(nvfp4_pack_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                       codes, N, K, T, chunks, reinterpret_cast<u32x4 *>(codes_packed));
+    hipLaunchKernelGGL(nvfp4_pack_scales_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
+                       scales, N, K, T, items, reinterpret_cast<u32x2 *>(scales_packed));
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X, uint16_t *Y,
+               int n, int N, int K, void *stream)
+{
+    int st = validate_common(Wq, Wscale, X, Y, n, N, K);
+    if (st != NVFP4_OK)
+        return st;
+    return launch_gemv(make_params(Wq, Wscale, gscale, X, Y, n, N, K), (hipStream_t)stream);
+}
+
+int nvfp4_gemv_qkv(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
+                   uint16_t *Y, int n, int K, const int32_t rows[3], const int64_t out_off[3],
+                   int64_t ldy, void *stream)
+{
+    if (!rows || !out_off)
+        return NVFP4_ERR_NULL;
+    long long N = 0;
+    for (int j = 0; j < 3; ++j) {
+        if (rows[j] < 0 || out_off[j] < 0 || out_off[j] + rows[j] > ldy)
+            return NVFP4_ERR_RANGE;
+        N += rows[j];
+    }
+    if (N < 1 || N > 0x7FFFFFFF)
+        return NVFP4_ERR_RANGE;
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (rows[a] > 0 && rows[b] > 0 && out_off[a] < out_off[b] + rows[b] &&
+                out_off[b] < out_off[a] + rows[a])
+                return NVFP4_ERR_RANGE;   // output ranges overlap
+    int st = validate_common(Wq, Wscale, X, Y, n, (int)N, K);
+    if (st != NVFP4_OK)
+        return st;
+    GemvParams p = make_params(Wq, Wscale, gscale, X, Y, n, (int)N, K);
+    p.start1 = rows[0];
+    p.start2 = rows[0] + rows[1];
+    p.off0 = out_off[0];
+    p.off1 = out_off[1];
+    p.off2 = out_off[2];
+    p.ldy = ldy;
+    return launch_gemv(p, (hipStream_t)stream);
+}
+
+int nvfp4_gemv_sched(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
+                     uint16_t *Y, int n, int N, int K, const uint8_t *tile_widths, int ntiles,
+                     void *stream)
+{
+    int st = validate_common(Wq, Wscale, X, Y, n, N, K);
+    if (st != NVFP4_OK)
+        return st;
+    st = check_schedule(n, tile_widths, ntiles);
+    if (st != NVFP4_OK)
+        return st;
+    int t0 = 0;
+    for (int j = 0; j < ntiles; ++j) {
+        GemvParams p = make_params(Wq, Wscale, gscale, X + (size_t)t0 * K, Y + (size_t)t0 * N,
+                                   tile_widths[j], N, K);
+        st = launch_gemv(p, (hipStream_t)stream);
+        if (st != NVFP4_OK)
+            return st;
+        t0 += tile_widths[j];
+    }
+    return NVFP4_OK;
+}
+
+int nvfp4_schedule(int n, int N, int K, uint8_t *widths, int max_tiles)
+{
+    if (!widths)
+        return -NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1)
+        return -NVFP4_ERR_RANGE;
+    if (max_tiles < 1)
+        return -NVFP4_ERR_SCHEDULE;
+    // One launch reads the weight once for every n <= 16; measured faster than
+    // any split into several launches at every shape (each extra tile re-reads
+    // the whole weight).
+    widths[0] = (uint8_t)n;
+    return 1;
+}
+
+int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles)
+{
+    if (!widths)
+        return -NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_TOKENS || width < 1 || width > NVFP4_MAX_TOKENS)
+        return -NVFP4_ERR_RANGE;
+    int cnt = 0, left = n;
+    while (left > 0) {
+        if (cnt >= max_tiles)
+            return -NVFP4_ERR_SCHEDULE;
+        const int w = left < width ? left : width;
+        widths[cnt++] = (uint8_t)w;
+        left -= w;
+    }
+    return cnt;
+}
+
+int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves, int *tiles_per_wave)
+{
+    if (!workgroups || !waves || !tiles_per_wave)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    int cus = 256;   // MI355X; the launch itself uses the queried count
+    Geometry geo;
+    if (!geometry_for(N, K, cus, &geo))
+        return NVFP4_ERR_SHAPE;
+    *workgroups = geo.workgroups;
+    *waves = geo.waves;
+    *tiles_per_wave = geo.mt;
+    return NVFP4_OK;
+}
+
+const char *nvfp4_strerror(int status)
+{
+    switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "null pointer argument";
+    case NVFP4_ERR_RANGE: return "argument out of range";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    case NVFP4_ERR_SHAPE: return "unsupported shape";
+    case NVFP4_ERR_SCHEDULE: return "invalid tile schedule";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    case NVFP4_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""Host-side checks of the HIP library (no GPU needed): the library loads and
+exports every symbol include/nvfp4.h declares, the pure host functions, and
+argument validation that must fail before any HIP call."""
+import ctypes
+
+import pytest
+
+import nvfp4_weight_only_02_amd as nv
+from nvfp4_weight_only_02_amd import metrics
+
+
+def test_library_exports_every_header_symbol():
+    names = nv.header_functions()
+    assert len(names) >= 11
+    L = nv.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror_names_every_status():
+    for code, name in nv.STATUS.items():
+        assert nv.strerror(code) and nv.strerror(code) != "unknown status"
+    assert nv.strerror(99) == "unknown status"
+
+
+def test_packed_sizes():
+    assert nv.packed_codes_bytes(16384, 5120) == 16384 * 5120 // 2
+    assert nv.packed_scales_bytes(16384, 5120) == 16384 * 5120 // 16
+    # rows padded to 16, K to 128
+    assert nv.packed_codes_bytes(17, 144) == 32 * 256 // 2
+    assert nv.packed_scales_bytes(17, 144) == 32 * 256 // 16
+    assert nv.packed_codes_bytes(16, 24) == 0 and nv.packed_codes_bytes(0, 16) == 0
+
+
+def test_greedy_schedule_pins_from_the_pages(golden):
+    case = golden["greedy_schedule"]
+    for n, tiles in zip(case["n"], case["tiles"]):
+        assert nv.schedule_greedy(n, 3) == tiles
+    assert len(nv.schedule_greedy(8, 3)) == 3          # n=8 costs 3 weight reads
+    assert len(nv.schedule_greedy(16, 3)) == 6
+
+
+def test_dispatcher_schedule_reads_weights_once():
+    for n in range(1, 17):
+        assert nv.schedule(n, 16384, 5120) == [n]
+    with pytest.raises(nv.Nvfp4Error):
+        nv.schedule(17, 16, 16)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.schedule_greedy(0, 3)
+
+
+def test_launch_geometry_fills_the_chip():
+    assert nv.launch_geometry(16, 16384, 5120) == (256, 8, 5)
+    assert nv.launch_geometry(1, 14336, 5120) == (256, 8, 5)
+    assert nv.launch_geometry(16, 5120, 6144) == (256, 8, 6)
+    assert nv.launch_geometry(1, 1024, 1024) == (64, 8, 1)
+    wg, waves, tpw = nv.launch_geometry(1, 37, 144)     # ragged: 3 row groups, 2 tiles
+    assert wg == 3 and waves * tpw >= 2
+
+
+def test_byte_model_matches_the_pages(golden):
+    b = golden["byte_model"]
+    assert metrics.algorithmic_bytes(b["n"], b["N"], b["K"]) == b["bytes"]
+    moved = b["us"] * 1e-6 * b["frac"] * b["GBps"] * 1e9
+    assert abs(moved / b["bytes"] - 1) < 1e-3
+
+
+FAKE = 0x100000   # 16-byte aligned, never dereferenced: every case below fails validation
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, FAKE, 1.0, FAKE, FAKE, 1, 16, 16), 1),          # null Wq
+    ((FAKE, FAKE, 1.0, 0, FAKE, 1, 16, 16), 1),          # null X
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 0, 16, 16), 2),       # n = 0
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 17, 16, 16), 2),      # n > 16
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 0, 16), 2),        # N = 0
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 24), 4),       # K % 16
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 8192 + 128), 4),  # K beyond the VGPR-resident X slice
+    ((FAKE + 8, FAKE, 1.0, FAKE, FAKE, 1, 16, 16), 3),   # Wq misaligned
+    ((FAKE, FAKE, 1.0, FAKE + 2, FAKE, 1, 16, 16), 3),   # X misaligned
+    ((FAKE, FAKE, 1.0, FAKE, FAKE + 1, 1, 16, 16), 3),   # Y misaligned
+])
+def test_gemv_validation(args, status):
+    assert nv.lib().nvfp4_gemv(*args, None) == status
+
+
+def test_qkv_validation():
+    L = nv.lib()
+    rows = (ctypes.c_int32 * 3)(32, 16, 16)
+    off = (ctypes.c_int64 * 3)(0, 32, 48)
+    assert L.nvfp4_gemv_qkv(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, None, off, 64, None) == 1
+    assert L.nvfp4_gemv_qkv(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, rows, off, 63, None) == 2   # ldy too small
+    overlap = (ctypes.c_int64 * 3)(0, 16, 48)
+    assert L.nvfp4_gemv_qkv(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, rows, overlap, 64, None) == 2
+    neg = (ctypes.c_int32 * 3)(32, -1, 16)
+    assert L.nvfp4_gemv_qkv(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, neg, off, 64, None) == 2
+    assert L.nvfp4_gemv_qkv(FAKE, FAKE, 1.0, FAKE, FAKE, 0, 16, rows, off, 64, None) == 2
+
+
+def test_sched_validation():
+    L = nv.lib()
+    bad = [(ctypes.c_uint8 * 2)(3, 3), 2, 5]       # widths sum to 6, n = 5
+    assert L.nvfp4_gemv_sched(FAKE, FAKE, 1.0, FAKE, FAKE, 5, 16, 16, bad[0], 2, None) == 5
+    zero = (ctypes.c_uint8 * 2)(5, 0)
+    assert L.nvfp4_gemv_sched(FAKE, FAKE, 1.0, FAKE, FAKE, 5, 16, 16, zero, 2, None) == 5
+    assert L.nvfp4_gemv_sched(FAKE, FAKE, 1.0, FAKE, FAKE, 5, 16, 16, None, 1, None) == 5
+    assert L.nvfp4_gemv_sched(FAKE, FAKE, 1.0, FAKE, FAKE, 5, 16, 24, zero, 2, None) == 4
+
+
+def test_quantize_and_pack_validation():
+    L = nv.lib()
+    assert L.nvfp4_quantize(0, 16, 16, FAKE, FAKE, FAKE, None) == 1
+    assert L.nvfp4_quantize(FAKE, 16, 24, FAKE, FAKE, FAKE, None) == 4
+    assert L.nvfp4_quantize(FAKE + 4, 16, 16, FAKE, FAKE, FAKE, None) == 3
+    assert L.nvfp4_quantize(FAKE, 0, 16, FAKE, FAKE, FAKE, None) == 2
+    assert L.nvfp4_pack(FAKE, FAKE, 16, 16, FAKE + 8, FAKE, None) == 3
+    assert L.nvfp4_pack(FAKE, 0, 16, 16, FAKE, FAKE, None) == 1
+    assert L.nvfp4_pack(FAKE, FAKE, 16, 20, FAKE, FAKE, None) == 4
