@@ -7,11 +7,10 @@
  *
  *     Y[t][r] = gscale * sum_k X[t][k] * e2m1(code[r][k]) * e4m3(scale[r][k/16])
  *
- * for t < n, r < N, reading the NVFP4 weight matrix once for all n tokens
- * instead of once per token (the tiling section of the same page: "each tile
- * reads the q/k/v/o projection weights ONCE for its tokens").  The page's
- * greedy 3-token tiling is available as an explicit schedule
- * (nvfp4_gemv_sched); the default launch reads the weights once for n <= 16.
+ * for t < n, r < N.  The page's point is that a tile of tokens shares one read
+ * of the weight matrix instead of one read per token; its greedy tiling into
+ * 3-token tiles is available as an explicit schedule (nvfp4_gemv_sched),
+ * while the default launch reads the weight once for all n <= 16 tokens.
  *
  * Number formats: the pages name NVFP4 without defining its bits.  Codes are
  * OCP FP4 E2M1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}), block scales OCP
@@ -90,7 +89,7 @@ int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K,
 
 /* Y[n][N] = X[n][K] . dequant(W)^T for 1 <= n <= 16 tokens.
  * Wq / Wscale: packed layout (nvfp4_pack), 16-byte aligned.
- * X: bf16 [n][K], 8-byte aligned.  Y: bf16 [n][N], 2-byte aligned.
+ * X: bf16 [n][K], 16-byte aligned.  Y: bf16 [n][N], 2-byte aligned.
  * Each token's result is bit-identical to the same token computed alone
  * (n = 1) and under any schedule of nvfp4_gemv_sched.
  * Errors: NULL, RANGE, SHAPE (K % 16), ALIGN, LAUNCH, DEVICE. */
@@ -128,10 +127,10 @@ int nvfp4_gemv_sched(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
  * negative status.  Pure host function. */
 int nvfp4_schedule(int n, int N, int K, uint8_t *widths, int max_tiles);
 
-/* The pages' greedy schedule: tiles of `width` tokens, then one remainder
- * tile (Atlas PR #266 description: "greedy 3s, then a 2-or-1 remainder"; n=8
- * costs 3 weight reads).  Returns the tile count or a negative status.  Pure
- * host function. */
+/* The pages' greedy schedule (Atlas PR #266 description): as many tiles of
+ * `width` tokens as fit, then one tile with the remaining tokens; with width 3
+ * a batch of 8 tokens takes 3 weight reads.  Returns the tile count or a
+ * negative status.  Pure host function. */
 int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles);
 
 /* Launch geometry the library uses for (n, N, K): workgroups, waves per

@@ -35,6 +35,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "../../include/nvfp4.h"
 
@@ -52,6 +53,9 @@ constexpr int kTileK = 128;            // K columns per tile (8 NVFP4 blocks)
 constexpr int kBlocksPerTile = kTileK / 16;
 constexpr int kMaxTilesPerWave = 8;    // X slice of a wave: 16 VGPRs per tile
 constexpr int kMaxWaves = 8;
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer resource: 32-bit data, no swizzle
+constexpr unsigned kOutOfRange = 0x7FFFFFF0u;   // buffer offset past any resource: reads zeros
+constexpr int kSlots = 8;                        // row-group partials parked in LDS
 
 struct GemvParams {
     const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
@@ -60,6 +64,7 @@ struct GemvParams {
     uint16_t *Y;           // bf16 output, token stride ldy
     float gscale;
     int n, N, K, T, RG;
+    int rg_base, rg_rem;   // row groups per workgroup: rg_base, +1 for the first rg_rem
     int start1, start2;    // first row of the 2nd and 3rd projection (N if absent)
     long long off0, off1, off2, ldy;
 };
@@ -88,15 +93,78 @@ __device__ __forceinline__ float fp8_to_f32(u32 w, int sel)
     }
 }
 
+// Calls f(std::integral_constant<int, j>) for j = 0 .. N-1.
+template <typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, J...>)
+{
+    (f(std::integral_constant<int, J>{}), ...);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A raw buffer resource over [base, base + bytes) (gfx9 layout: 48-bit base,
+// stride 0, byte-granular range check).
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, unsigned bytes)
+{
+    const unsigned long long a = (unsigned long long)base;
+    return u32x4{(u32)a, (u32)(a >> 32) & 0xFFFFu, bytes, (u32)kBufferWord3};
+}
+
+// Loads whose completion is tracked by hand (see the vmcnt bookkeeping in
+// the kernel).  Offsets past the resource's range return zeros.
+__device__ __forceinline__ u32x4 buffer_load_b128(u32x4 rsrc, unsigned off)
+{
+    u32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+__device__ __forceinline__ u32x4 buffer_load_b128_nt(u32x4 rsrc, unsigned off)
+{
+    u32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen nt" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+__device__ __forceinline__ u32x2 buffer_load_b64_nt(u32x4 rsrc, unsigned off)
+{
+    u32x2 v;
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+// Wait until at most N vector-memory operations are outstanding; the
+// registers passed are the ones the wait makes valid (tied in and out, so no
+// read of them can be scheduled before it).
+template <int N>
+__device__ __forceinline__ void vm_wait2(u32x4 &a, u32x2 &b, std::integral_constant<int, N>)
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait4(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d, std::integral_constant<int, N>)
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 {
     return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: RNE
 }
 
 // One launch covers every token (n <= 16) of one weight matrix.
-//   W  waves per workgroup, each owning a contiguous K-slice of MT tiles;
-//   EXACT: every wave owns exactly MT tiles (T == W * MT), no predication.
-template <int W, int MT, bool EXACT>
+//   W     waves per workgroup, each owning a contiguous K-slice of MT tiles;
+//   PFD   row groups of weight tiles each wave keeps in flight (1 or 2);
+//   EXACT every wave owns exactly MT tiles (K == 128 * T, T == W * MT), so
+//         no column predication is needed.
+template <int W, int MT, int PFD, bool EXACT>
 __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
 {
     const int lane = threadIdx.x & 63;
@@ -104,80 +172,112 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
     const int i = lane & 15;   // token row of A, weight row of B and C
     const int g = lane >> 4;   // K quarter of A and B, token quarter of C
 
-    const int rg0 = (int)(((unsigned long long)blockIdx.x * (unsigned)p.RG) / gridDim.x);
-    const int rg1 = (int)(((unsigned long long)(blockIdx.x + 1) * (unsigned)p.RG) / gridDim.x);
+    const int wg = blockIdx.x;
+    const int rg0 = wg * p.rg_base + min(wg, p.rg_rem);
+    const int rg1 = rg0 + p.rg_base + (wg < p.rg_rem ? 1 : 0);
     const int tw0 = wave * MT;
     const int tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
 
-    // This wave's K-slice of X, in MFMA A-operand layout: lane (i, g) holds
-    // X[i][k .. k+3] with k = 16*block + 4*g, for every block of the slice.
-    // Lanes of tokens >= n load token 0's values and zero them.  When the
-    // slices tile K exactly (EXACT, K == 128*T) no column check is needed and
-    // all loads share one base address with immediate offsets.
+    // All vector-memory loads of the main path are issued as inline buffer
+    // loads and waited for with explicit, compile-time vmcnt values: loads
+    // retire in issue order, so "at most N newer loads outstanding" is exact
+    // bookkeeping, and every read of a loaded register goes through the wait
+    // statement (its operands are tied), so nothing reads a register whose
+    // load is still in flight.  (The compiler's own wait insertion drains the
+    // whole weight ring at the loop back-edge once two row groups are in
+    // flight.)
+    //
+    // Issue order: this wave's X slice first (it is cache-resident after the
+    // first workgroups touch it), then PFD row groups of weight tiles, so the
+    // X staging below never waits for an HBM load.
+    //
+    // Buffer resources: X ends at row n, the weights at this workgroup's last
+    // row group; loads past the end (tokens >= n, the prefetch beyond the
+    // last row group) return zeros without a memory access.
+    const unsigned nrg = (unsigned)(rg1 - rg0);
+    const u32x4 crsrc = buffer_rsrc(p.codes + (size_t)rg0 * p.T * 64, nrg * p.T * 1024u);
+    const u32x4 srsrc = buffer_rsrc(p.scales + (size_t)rg0 * p.T * 16, nrg * p.T * 128u);
+    const u32x4 xrsrc = buffer_rsrc(p.X, (unsigned)(p.n * p.K * 2));
+    auto load_tile = [&](int rgl, int t, u32x4 &c, u32x2 &s) {
+        const bool ok = EXACT || t < tw;
+        const unsigned tile = (unsigned)(rgl * p.T + tw0 + t);
+        const unsigned co = ok ? tile * 1024u + (unsigned)lane * 16u : kOutOfRange;
+        const unsigned so = ok ? tile * 128u + (unsigned)i * 8u : kOutOfRange;
+        c = buffer_load_b128_nt(crsrc, co);
+        s = buffer_load_b64_nt(srsrc, so);
+    };
+
+    // X: lane (chunk, q) loads the 16-byte chunk `chunk` of token row
+    // q*4 + lane/16 of each tile of the slice (16 lanes cover one row's 256
+    // bytes: whole-line loads).
+    constexpr int kStageRow = kTileK * 2 / 16 + 1;   // 16-byte chunks per row, +1 pad
+    __shared__ u32x4 xstage[W][kRowsPerGroup][kStageRow];
+    const int chunk = lane & 15;
+    u32x4 xg[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = q * 4 + (lane >> 4);
+            const int k = (tw0 + t) * kTileK + chunk * 8;
+            const bool ok = row < p.n && (EXACT || k < p.K);
+            xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
+        }
+
+    // Weight tiles in flight: ring set d holds the tiles of row group
+    // rg0 + d (+ PFD per round); slot t is refilled as soon as it is consumed.
+    u32x4 wc[PFD][MT];
+    u32x2 ws[PFD][MT];
+#pragma unroll
+    for (int d = 0; d < PFD; ++d)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            load_tile(d, t, wc[d][t], ws[d][t]);
+
+    // Stage X through a per-wave LDS tile into MFMA A-operand layout: lane
+    // (i, g) holds X[i][k .. k+3] with k = 16*block + 4*g, for every block of
+    // the slice.  Tile t's 4 loads have 4*(MT-1-t) X loads and 2*PFD*MT
+    // weight loads issued after them.
     u32x2 xr[MT][kBlocksPerTile];
-    const bool tok_ok = i < p.n;
-    const uint16_t *xrow = p.X + (size_t)(tok_ok ? i : 0) * p.K + 4 * g;
-    if constexpr (EXACT) {
-        const u32x2 *xp = reinterpret_cast<const u32x2 *>(xrow + tw0 * kTileK);
+    static_for<MT>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3],
+                 std::integral_constant<int, 4 * (MT - 1 - t) + 2 * PFD * MT>{});
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int q = 0; q < 4; ++q)
+            xstage[wave][q * 4 + (lane >> 4)][chunk] = xg[t][q];
+        const char *base = reinterpret_cast<const char *>(&xstage[wave][i][0]);
 #pragma unroll
-            for (int b = 0; b < kBlocksPerTile; ++b)
-                xr[t][b] = xp[(t * kTileK + b * 16) / 4];
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int b = 0; b < kBlocksPerTile; ++b)
-                xr[t][b] = tok_ok ? xr[t][b] : u32x2{0u, 0u};
-    } else {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-#pragma unroll
-            for (int b = 0; b < kBlocksPerTile; ++b) {
-                const int k = ((tw0 + t) * kBlocksPerTile + b) * 16;
-                const bool ok = tok_ok && t < tw && k + 4 * g < p.K;
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(xrow + (ok ? k : 0));
-                xr[t][b] = ok ? v : u32x2{0u, 0u};
-            }
-        }
-    }
+        for (int b = 0; b < kBlocksPerTile; ++b)
+            xr[t][b] = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
+    });
 
-    // Weight tiles in flight: slot t holds tile t of the current row group's
-    // slice until it is consumed, then the same tile of the next row group.
-    // Every workgroup owns at least one row group (the host launches at most
-    // RG workgroups), so the first tiles are loaded unconditionally, in slot
-    // order, as the loop body reloads them.
-    u32x4 wc[MT];
-    u32x2 ws[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        wc[t] = u32x4{0u, 0u, 0u, 0u};
-        ws[t] = u32x2{0u, 0u};
-        if (EXACT || t < tw) {
-            const size_t tile = (size_t)rg0 * p.T + tw0 + t;
-            wc[t] = __builtin_nontemporal_load(p.codes + tile * 64 + lane);
-            ws[t] = __builtin_nontemporal_load(p.scales + tile * 16 + i);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    __shared__ f32x4 part[2][W][64];
+    // Partial sums of up to kSlots row groups wait in LDS and are reduced
+    // together, so waves only meet at a barrier once per kSlots row groups
+    // (once per launch at the decode shapes) instead of after every row group.
+    __shared__ f32x4 part[kSlots][W][64];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    // One row group of this wave's K-slice.  PF: refill each ring slot with
-    // the next row group's tile as soon as the slot is read.  Blocks run as a
-    // software pipeline (the scale FMA of a block trails its MFMA by two
-    // blocks); scheduling barriers keep the compiler from hoisting all MFMAs
-    // ahead of their FMAs, which would hold every partial in registers.
-    auto rowgroup = [&](auto pf_tag, int rg) -> f32x4 {
-        constexpr bool PF = decltype(pf_tag)::value;
+    // One row group of this wave's K-slice from ring set D; each slot is
+    // refilled with the same tile PFD row groups ahead once it is consumed.
+    // Every wave runs all MT slots (tiles past the end of K were loaded as
+    // zeros), so the number of loads per round, and with it the wait counts,
+    // is the same for every wave.
+    // Blocks run as a software pipeline (the scale FMA of a block trails its
+    // MFMA by two blocks).
+    auto rowgroup = [&](auto set_tag, int rg) -> f32x4 {
+        constexpr int D = decltype(set_tag)::value;
         f32x4 acc = zero, p1 = zero, p2 = zero;
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            if (EXACT || t < tw) {
-                const u32x4 c = wc[t];
-                const u32x2 s = ws[t];
+            {
+                // Every slot has 2*PFD*MT - 1 loads issued after its codes
+                // and 2*PFD*MT - 2 after its scales (stores of Y issued in
+                // between only make the wait stricter).
+                vm_wait2(wc[D][t], ws[D][t], std::integral_constant<int, 2 * PFD * MT - 2>{});
+                const u32x4 c = wc[D][t];
+                const u32x2 s = ws[D][t];
 #pragma unroll
                 for (int b = 0; b < kBlocksPerTile; ++b) {
                     // B operand: W[row i][16*block + 4*g + e], e = 0..3, from
@@ -203,13 +303,10 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
                     asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
                 }
                 // Refill the slot once its codes and scales are consumed, so
-                // the next tile lands in the same registers (no copy, and no
-                // wait on the other slots at the top of the next row group).
-                if constexpr (PF) {
-                    const size_t tile = (size_t)(rg + 1) * p.T + tw0 + t;
-                    wc[t] = __builtin_nontemporal_load(p.codes + tile * 64 + lane);
-                    ws[t] = __builtin_nontemporal_load(p.scales + tile * 16 + i);
-                }
+                // the next tile lands in the same registers.  The scheduling
+                // barrier keeps later tiles' work (and so their waits on
+                // loads still in flight) below this point.
+                load_tile(rg - rg0 + PFD, t, wc[D][t], ws[D][t]);
             }
         }
 #pragma unroll
@@ -218,46 +315,62 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
         return acc;
     };
 
-    // Sum the K-slices of row group rg in wave order 0..W-1 and store it.
-    auto finish = [&](int rg, const f32x4 acc) {
-        part[rg & 1][wave][lane] = acc;
-        __syncthreads();
-        if (wave == (rg - rg0) % W) {
-            f32x4 sum = part[rg & 1][0][lane];
+    // Sum the K-slices of row group rg in wave order 0..W-1, scale by gscale,
+    // round to bf16 and store the row group's outputs.
+    auto reduce_store = [&](int rg, int slot) {
+        f32x4 sum = part[slot][0][lane];
 #pragma unroll
-            for (int w = 1; w < W; ++w) {
-                const f32x4 q = part[rg & 1][w][lane];
-                sum[0] = sum[0] + q[0];
-                sum[1] = sum[1] + q[1];
-                sum[2] = sum[2] + q[2];
-                sum[3] = sum[3] + q[3];
-            }
-            const int r = rg * kRowsPerGroup + i;
-            if (r < p.N) {
-                long long off;
-                if (r >= p.start2)
-                    off = p.off2 + (r - p.start2);
-                else if (r >= p.start1)
-                    off = p.off1 + (r - p.start1);
-                else
-                    off = p.off0 + r;
+        for (int w = 1; w < W; ++w) {
+            const f32x4 q = part[slot][w][lane];
+            sum[0] = sum[0] + q[0];
+            sum[1] = sum[1] + q[1];
+            sum[2] = sum[2] + q[2];
+            sum[3] = sum[3] + q[3];
+        }
+        const int r = rg * kRowsPerGroup + i;
+        if (r < p.N) {
+            long long off;
+            if (r >= p.start2)
+                off = p.off2 + (r - p.start2);
+            else if (r >= p.start1)
+                off = p.off1 + (r - p.start1);
+            else
+                off = p.off0 + r;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int tok = 4 * g + v;
-                    if (tok < p.n)
-                        p.Y[(long long)tok * p.ldy + off] = f32_to_bf16_bits(p.gscale * sum[v]);
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 4 * g + v;
+                if (tok < p.n)
+                    p.Y[(long long)tok * p.ldy + off] = f32_to_bf16_bits(p.gscale * sum[v]);
             }
         }
     };
 
-    // Every row group but the last prefetches its successor; the last one is
-    // peeled so both loop bodies are straight-line code.
-    int rg = rg0;
-    for (; rg + 1 < rg1; ++rg)
-        finish(rg, rowgroup(std::true_type{}, rg));
-    if (rg < rg1)
-        finish(rg, rowgroup(std::false_type{}, rg));
+    // Park the partial of row group rg; when the slots are full or the last
+    // row group is in, reduce them (slot s by wave s % W) between barriers.
+    auto finish = [&](int rg, const f32x4 acc) {
+        const int slot = (rg - rg0) % kSlots;
+        part[slot][wave][lane] = acc;
+        if (slot == kSlots - 1 || rg == rg1 - 1) {
+            __syncthreads();
+            const int base = rg - slot;
+            for (int sl = wave; sl <= slot; sl += W)
+                reduce_store(base + sl, sl);
+            if (rg != rg1 - 1)
+                __syncthreads();
+        }
+    };
+
+    // With two ring sets the loop always runs both halves (past the last row
+    // group the ring holds zeros from out-of-range loads and the result is
+    // dropped), so the loop has a single exit and every wait count is exact.
+    for (int rg = rg0; rg < rg1; rg += PFD) {
+        finish(rg, rowgroup(std::integral_constant<int, 0>{}, rg));
+        if constexpr (PFD == 2) {
+            const f32x4 acc = rowgroup(std::integral_constant<int, 1>{}, rg + 1);
+            if (rg + 1 < rg1)
+                finish(rg + 1, acc);
+        }
+    }
 }
 
 // ---- pack: canonical -> tiled device layout --------------------------------
@@ -416,39 +529,48 @@ __global__ void nvfp4_quantize_kernel(const float4 *W, long long nblocks, uint2 
 
 typedef void (*GemvKernel)(GemvParams);
 
-template <int W, int MT>
+template <int W, int MT, int PFD>
 GemvKernel pick_exact(bool exact)
 {
-    return exact ? nvfp4_gemv_kernel<W, MT, true> : nvfp4_gemv_kernel<W, MT, false>;
+    if constexpr (PFD == 2 && MT > 6)
+        return nullptr;   // two row groups of 7-8 tiles do not fit the VGPR budget
+    else
+        return exact ? nvfp4_gemv_kernel<W, MT, PFD, true> : nvfp4_gemv_kernel<W, MT, PFD, false>;
 }
 
-template <int W>
+template <int W, int PFD>
 GemvKernel pick_mt(int mt, bool exact)
 {
     switch (mt) {
-    case 1: return pick_exact<W, 1>(exact);
-    case 2: return pick_exact<W, 2>(exact);
-    case 3: return pick_exact<W, 3>(exact);
-    case 4: return pick_exact<W, 4>(exact);
-    case 5: return pick_exact<W, 5>(exact);
-    case 6: return pick_exact<W, 6>(exact);
-    case 7: return pick_exact<W, 7>(exact);
-    default: return pick_exact<W, 8>(exact);
+    case 1: return pick_exact<W, 1, PFD>(exact);
+    case 2: return pick_exact<W, 2, PFD>(exact);
+    case 3: return pick_exact<W, 3, PFD>(exact);
+    case 4: return pick_exact<W, 4, PFD>(exact);
+    case 5: return pick_exact<W, 5, PFD>(exact);
+    case 6: return pick_exact<W, 6, PFD>(exact);
+    case 7: return pick_exact<W, 7, PFD>(exact);
+    default: return pick_exact<W, 8, PFD>(exact);
     }
 }
 
-GemvKernel pick_kernel(int waves, int mt, bool exact)
+template <int PFD>
+GemvKernel pick_w(int waves, int mt, bool exact)
 {
     switch (waves) {
-    case 1: return pick_mt<1>(mt, exact);
-    case 2: return pick_mt<2>(mt, exact);
-    case 4: return pick_mt<4>(mt, exact);
-    default: return pick_mt<8>(mt, exact);
+    case 1: return pick_mt<1, PFD>(mt, exact);
+    case 2: return pick_mt<2, PFD>(mt, exact);
+    case 4: return pick_mt<4, PFD>(mt, exact);
+    default: return pick_mt<8, PFD>(mt, exact);
     }
+}
+
+GemvKernel pick_kernel(int waves, int mt, int pfd, bool exact)
+{
+    return pfd == 2 ? pick_w<2>(waves, mt, exact) : pick_w<1>(waves, mt, exact);
 }
 
 struct Geometry {
-    int workgroups, waves, mt;
+    int workgroups, waves, mt, pfd;
     bool exact;
 };
 
@@ -497,6 +619,7 @@ bool geometry_for(int N, int K, int cus, Geometry *geo)
         geo->waves = kMaxWaves;
         geo->mt = (T + kMaxWaves - 1) / kMaxWaves;
     }
+    geo->pfd = geo->mt <= 6 ? 2 : 1;   // a second row group in flight fits the VGPR budget
     const int per_cu = geo->waves >= 8 ? 1 : 8 / geo->waves;
     long long wg = (long long)cus * per_cu;
     geo->workgroups = (int)(RG < wg ? RG : wg);
@@ -520,7 +643,7 @@ int validate_common(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X,
     const int T = (K + kTileK - 1) / kTileK;
     if ((T + kMaxWaves - 1) / kMaxWaves > kMaxTilesPerWave)
         return NVFP4_ERR_SHAPE;   // K > 8192: the X slice would not fit in VGPRs
-    if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 8) || !aligned(Y, 2))
+    if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 16) || !aligned(Y, 2))
         return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
 }
@@ -534,8 +657,13 @@ int launch_gemv(const GemvParams &p, hipStream_t stream)
     Geometry geo;
     if (!geometry_for(p.N, p.K, cus, &geo))
         return NVFP4_ERR_SHAPE;
-    GemvKernel k = pick_kernel(geo.waves, geo.mt, geo.exact);
-    hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(geo.waves * 64), 0, stream, p);
+    GemvKernel k = pick_kernel(geo.waves, geo.mt, geo.pfd, geo.exact);
+    if (!k)
+        return NVFP4_ERR_SHAPE;
+    GemvParams q = p;
+    q.rg_base = p.RG / geo.workgroups;
+    q.rg_rem = p.RG % geo.workgroups;
+    hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(geo.waves * 64), 0, stream, q);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

@@ -78,6 +78,7 @@ FAKE = 0x100000   # 16-byte aligned, never dereferenced: every case below fails 
     ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 8192 + 128), 4),  # K beyond the VGPR-resident X slice
     ((FAKE + 8, FAKE, 1.0, FAKE, FAKE, 1, 16, 16), 3),   # Wq misaligned
     ((FAKE, FAKE, 1.0, FAKE + 2, FAKE, 1, 16, 16), 3),   # X misaligned
+    ((FAKE, FAKE, 1.0, FAKE + 8, FAKE, 1, 16, 16), 3),   # X not 16-byte aligned
     ((FAKE, FAKE, 1.0, FAKE, FAKE + 1, 1, 16, 16), 3),   # Y misaligned
 ])
 def test_gemv_validation(args, status):
