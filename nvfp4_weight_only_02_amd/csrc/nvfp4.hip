@@ -619,7 +619,7 @@ bool geometry_for(int N, int K, int cus, Geometry *geo)
         geo->waves = kMaxWaves;
         geo->mt = (T + kMaxWaves - 1) / kMaxWaves;
     }
-    geo->pfd = geo->mt <= 6 ? 2 : 1;   // a second row group in flight fits the VGPR budget
+    geo->pfd = 1;   // measured: a second row group in flight is slower at every decode shape
     const int per_cu = geo->waves >= 8 ? 1 : 8 / geo->waves;
     long long wg = (long long)cus * per_cu;
     geo->workgroups = (int)(RG < wg ? RG : wg);
