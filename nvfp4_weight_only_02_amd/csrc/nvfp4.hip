@@ -371,6 +371,17 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
                 finish(rg + 1, acc);
         }
     }
+
+    // The last round's refills (zeros from past the end) are never read, but
+    // the hardware still writes their registers when they return.  Wait for
+    // them with the ring registers tied, so the compiler cannot hand those
+    // registers to other values while the loads are in flight.
+    static_for<PFD>([&](auto dc) {
+        static_for<MT>([&](auto tc) {
+            vm_wait2(wc[decltype(dc)::value][decltype(tc)::value], ws[decltype(dc)::value][decltype(tc)::value],
+                     std::integral_constant<int, 0>{});
+        });
+    });
 }
 
 // ---- pack: canonical -> tiled device layout --------------------------------
