@@ -9,22 +9,32 @@
 // Design (gfx950-first; the pages' CUDA kernels are prior art only):
 //  * Packed layout: 16-row x 128-column tiles.  A tile's 1 KiB of codes is one
 //    16-byte load per lane of a 64-lane wavefront, laid out so that the bytes a
-//    lane loads are exactly the MFMA operand fragments it feeds; the tile's 128
-//    scale bytes are one 8-byte load per row.
+//    lane loads are exactly the MFMA operand fragments it feeds.  A wave's
+//    block scales for one row group (its tiles' 128-byte scale rows, contiguous)
+//    are one 16-byte load per lane, passed to the lanes that need them through
+//    a small per-wave LDS buffer.
 //  * Dequant in registers: v_cvt_scalef32_pk_bf16_fp4 turns two E2M1 codes into
 //    two exact bf16 values per instruction.  The E4M3 block scale is NOT folded
 //    into that conversion (the hardware applies only the exponent of its f32
 //    scale operand); instead each 16-element K-block is one
 //    v_mfma_f32_16x16x16_bf16 whose fp32 partial is multiplied by the block
 //    scale with one fp32 FMA per output.
-//  * Tokens are the MFMA M dimension, padded to 16: every n runs the identical
-//    instruction sequence, so a token's result never depends on n or on the
-//    other tokens of the launch (bit-identity with the n = 1 result).
-//  * Persistent workgroups: each wave owns a fixed K-slice; its slice of X sits
-//    in VGPRs for the whole launch (loaded once, straight in MFMA A-operand
-//    layout), and it streams the weight tiles of its slice for consecutive
-//    16-row groups, prefetching the next row group's tiles while it computes
-//    the current one, so loads stay in flight across the dequant work.
+//  * Tokens are the MFMA M dimension, padded to 16, token t on MFMA row
+//    4*(t%4) + t/4.  Accumulator component v of a lane then holds tokens
+//    4v..4v+3, so a launch of n tokens runs the scale FMAs of the first
+//    ceil(n/4) components only.  A token always sits on the same MFMA row and
+//    its component runs the same instruction sequence whatever n is, so its
+//    result never depends on n or on the other tokens (bit-identity with the
+//    n = 1 result).
+//  * Persistent workgroups, 8 waves each, one contiguous range of row groups
+//    per workgroup with the ranges as even as the chip allows (every
+//    workgroup runs the same number of rounds).  Each wave owns a fixed
+//    K-slice; its slice of X sits in VGPRs for the whole launch (loaded once,
+//    straight in MFMA A-operand layout, load instructions for token rows >= n
+//    skipped), and it streams the weight tiles of its slice for consecutive
+//    16-row groups, refilling each ring slot with the next row group's tile as
+//    soon as it is consumed (a ring of one row group: measured faster than
+//    deeper rings, whose loads return later and stall the compute behind them).
 //  * K-slice partials are summed through LDS in a fixed wave order, then
 //    scaled by gscale and rounded to bf16 (RNE) in the epilogue, which writes
 //    each projection's rows straight to its output offset (fused QKV).
@@ -52,7 +62,7 @@ constexpr int kRowsPerGroup = 16;      // MFMA N dimension: weight rows per tile
 constexpr int kTileK = 128;            // K columns per tile (8 NVFP4 blocks)
 constexpr int kBlocksPerTile = kTileK / 16;
 constexpr int kMaxTilesPerWave = 8;    // X slice of a wave: 16 VGPRs per tile
-constexpr int kMaxWaves = 8;
+constexpr int kWaves = 8;            // waves per workgroup, one K-slice each
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer resource: 32-bit data, no swizzle
 constexpr unsigned kOutOfRange = 0x7FFFFFF0u;   // buffer offset past any resource: reads zeros
 constexpr int kSlots = 8;                        // row-group partials parked in LDS
@@ -80,17 +90,6 @@ __device__ __forceinline__ u32 fp4x2_to_bf16x2(u32 w, int sel)
     default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3); break;
     }
     return __builtin_bit_cast(u32, v);
-}
-
-// E4M3FN byte `sel` of w -> f32 (exact; gfx950 decodes the OCP encoding).
-__device__ __forceinline__ float fp8_to_f32(u32 w, int sel)
-{
-    switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
-    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-    }
 }
 
 // Calls f(std::integral_constant<int, j>) for j = 0 .. N-1.
@@ -130,23 +129,9 @@ __device__ __forceinline__ u32x4 buffer_load_b128_nt(u32x4 rsrc, unsigned off)
     return v;
 }
 
-__device__ __forceinline__ u32x2 buffer_load_b64_nt(u32x4 rsrc, unsigned off)
-{
-    u32x2 v;
-    asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(v) : "v"(off), "s"(rsrc));
-    return v;
-}
-
 // Wait until at most N vector-memory operations are outstanding; the
 // registers passed are the ones the wait makes valid (tied in and out, so no
 // read of them can be scheduled before it).
-template <int N>
-__device__ __forceinline__ void vm_wait2(u32x4 &a, u32x2 &b, std::integral_constant<int, N>)
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
-}
-
 template <int N>
 __device__ __forceinline__ void vm_wait4(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d, std::integral_constant<int, N>)
 {
@@ -159,18 +144,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
     return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: RNE
 }
 
-// One launch covers every token (n <= 16) of one weight matrix.
-//   W     waves per workgroup, each owning a contiguous K-slice of MT tiles;
-//   PFD   row groups of weight tiles each wave keeps in flight (1 or 2);
-//   EXACT every wave owns exactly MT tiles (K == 128 * T, T == W * MT), so
-//         no column predication is needed.
-template <int W, int MT, int PFD, bool EXACT>
-__global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
+template <int N>
+__device__ __forceinline__ void vm_wait1(u32x4 &a, std::integral_constant<int, N>)
 {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(a) : "n"(N));
+}
+
+// One launch covers every token (n <= 16) of one weight matrix.
+//   MT    tiles of the K-slice each of the kWaves waves owns;
+//   NV    ceil(n / 4): accumulator components that carry real tokens;
+//   EXACT every wave owns exactly MT tiles (K == 128 * T, T == kWaves * MT),
+//         so no column predication is needed.
+template <int MT, int NV, bool EXACT>
+__global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
+{
+    constexpr int W = kWaves;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int i = lane & 15;   // token row of A, weight row of B and C
-    const int g = lane >> 4;   // K quarter of A and B, token quarter of C
+    const int i = lane & 15;   // MFMA row of A (token 4*(i%4) + i/4), weight row of B and C
+    const int g = lane >> 4;   // K quarter of A and B, accumulator token offset of C
 
     const int wg = blockIdx.x;
     const int rg0 = wg * p.rg_base + min(wg, p.rg_rem);
@@ -178,75 +171,71 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
     const int tw0 = wave * MT;
     const int tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
 
-    // All vector-memory loads of the main path are issued as inline buffer
-    // loads and waited for with explicit, compile-time vmcnt values: loads
-    // retire in issue order, so "at most N newer loads outstanding" is exact
-    // bookkeeping, and every read of a loaded register goes through the wait
-    // statement (its operands are tied), so nothing reads a register whose
-    // load is still in flight.  (The compiler's own wait insertion drains the
-    // whole weight ring at the loop back-edge once two row groups are in
-    // flight.)
-    //
-    // Issue order: this wave's X slice first (it is cache-resident after the
-    // first workgroups touch it), then PFD row groups of weight tiles, so the
-    // X staging below never waits for an HBM load.
-    //
-    // Buffer resources: X ends at row n, the weights at this workgroup's last
-    // row group; loads past the end (tokens >= n, the prefetch beyond the
-    // last row group) return zeros without a memory access.
+    // All vector-memory loads of the main path are inline buffer loads waited
+    // for with explicit, compile-time vmcnt values: loads retire in issue
+    // order, so "at most N newer loads outstanding" is exact bookkeeping, and
+    // every read of a loaded register goes through the wait statement (its
+    // operands are tied), so nothing reads a register whose load is still in
+    // flight.  Buffer resources: X ends at row n, the weights at this
+    // workgroup's last row group; loads past the end return zeros without a
+    // memory access.
     const unsigned nrg = (unsigned)(rg1 - rg0);
     const u32x4 crsrc = buffer_rsrc(p.codes + (size_t)rg0 * p.T * 64, nrg * p.T * 1024u);
-    const u32x4 srsrc = buffer_rsrc(p.scales + (size_t)rg0 * p.T * 16, nrg * p.T * 128u);
+    const u32x4 srsrc = buffer_rsrc(reinterpret_cast<const char *>(p.scales) + (size_t)rg0 * p.T * 128,
+                                    nrg * p.T * 128u);
     const u32x4 xrsrc = buffer_rsrc(p.X, (unsigned)(p.n * p.K * 2));
-    auto load_tile = [&](int rgl, int t, u32x4 &c, u32x2 &s) {
-        const bool ok = EXACT || t < tw;
-        const unsigned tile = (unsigned)(rgl * p.T + tw0 + t);
-        const unsigned co = ok ? tile * 1024u + (unsigned)lane * 16u : kOutOfRange;
-        const unsigned so = ok ? tile * 128u + (unsigned)i * 8u : kOutOfRange;
-        c = buffer_load_b128_nt(crsrc, co);
-        s = buffer_load_b64_nt(srsrc, so);
-    };
 
-    // X: lane (chunk, q) loads the 16-byte chunk `chunk` of token row
-    // q*4 + lane/16 of each tile of the slice (16 lanes cover one row's 256
-    // bytes: whole-line loads).
+    // X first (it is cache-resident after the first workgroups touch it, so
+    // its staging below never waits for an HBM load): lane (chunk, q) loads
+    // the 16-byte chunk `chunk` of token row q*4 + lane/16 of each tile of
+    // the slice (16 lanes cover one row's 256 bytes: whole-line loads).  Load
+    // instructions whose four token rows are all >= n are not issued.
     constexpr int kStageRow = kTileK * 2 / 16 + 1;   // 16-byte chunks per row, +1 pad
     __shared__ u32x4 xstage[W][kRowsPerGroup][kStageRow];
     const int chunk = lane & 15;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
     u32x4 xg[MT][4];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int row = q * 4 + (lane >> 4);
-            const int k = (tw0 + t) * kTileK + chunk * 8;
-            const bool ok = row < p.n && (EXACT || k < p.K);
-            xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
+            xg[t][q] = z4;
+            if (4 * q < p.n) {
+                const int row = q * 4 + (lane >> 4);
+                const int k = (tw0 + t) * kTileK + chunk * 8;
+                const bool ok = row < p.n && (EXACT || k < p.K);
+                xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
+            }
         }
 
-    // Weight tiles in flight: ring set d holds the tiles of row group
-    // rg0 + d (+ PFD per round); slot t is refilled as soon as it is consumed.
-    u32x4 wc[PFD][MT];
-    u32x2 ws[PFD][MT];
+    // Weight ring: one row group of this wave's K-slice, issued as
+    // [scale chunk, code tile 0 .. MT-1].  The scale chunk is the MT * 128
+    // contiguous scale bytes of the slice (lane l holds bytes 16l .. 16l+15).
+    u32x4 wsc;
+    u32x4 wc[MT];
+    auto scale_off = [&](int rgl) -> unsigned {
+        return lane < 8 * tw ? (unsigned)((rgl * p.T + tw0) * 128 + lane * 16) : kOutOfRange;
+    };
+    auto code_off = [&](int rgl, int t) -> unsigned {
+        return (EXACT || t < tw) ? (unsigned)((rgl * p.T + tw0 + t) * 1024 + lane * 16) : kOutOfRange;
+    };
+    wsc = buffer_load_b128_nt(srsrc, scale_off(0));
 #pragma unroll
-    for (int d = 0; d < PFD; ++d)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            load_tile(d, t, wc[d][t], ws[d][t]);
+    for (int t = 0; t < MT; ++t)
+        wc[t] = buffer_load_b128_nt(crsrc, code_off(0, t));
 
     // Stage X through a per-wave LDS tile into MFMA A-operand layout: lane
-    // (i, g) holds X[i][k .. k+3] with k = 16*block + 4*g, for every block of
-    // the slice.  Tile t's 4 loads have 4*(MT-1-t) X loads and 2*PFD*MT
-    // weight loads issued after them.
+    // (i, g) holds X[4*(i%4) + i/4][k .. k+3] with k = 16*block + 4*g, for
+    // every block of the slice.  Every X load is older than the MT + 1 ring
+    // loads.
     u32x2 xr[MT][kBlocksPerTile];
     static_for<MT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3],
-                 std::integral_constant<int, 4 * (MT - 1 - t) + 2 * PFD * MT>{});
+        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, MT + 1>{});
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             xstage[wave][q * 4 + (lane >> 4)][chunk] = xg[t][q];
-        const char *base = reinterpret_cast<const char *>(&xstage[wave][i][0]);
+        const char *base = reinterpret_cast<const char *>(&xstage[wave][4 * (i & 3) + (i >> 2)][0]);
 #pragma unroll
         for (int b = 0; b < kBlocksPerTile; ++b)
             xr[t][b] = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
@@ -256,76 +245,82 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
     // together, so waves only meet at a barrier once per kSlots row groups
     // (once per launch at the decode shapes) instead of after every row group.
     __shared__ f32x4 part[kSlots][W][64];
+    __shared__ u32x4 sstage[W][64];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    // One row group of this wave's K-slice from ring set D; each slot is
-    // refilled with the same tile PFD row groups ahead once it is consumed.
-    // Every wave runs all MT slots (tiles past the end of K were loaded as
-    // zeros), so the number of loads per round, and with it the wait counts,
-    // is the same for every wave.
+    // One row group of this wave's K-slice.  REFILL: each ring slot is
+    // refilled with the same slot of the next row group as soon as it is
+    // consumed, so every wait has exactly MT newer loads (the ring); on the
+    // last row group nothing is refilled and the counts fall as it drains.
     // Blocks run as a software pipeline (the scale FMA of a block trails its
     // MFMA by two blocks).
-    auto rowgroup = [&](auto set_tag, int rg) -> f32x4 {
-        constexpr int D = decltype(set_tag)::value;
+    auto rowgroup = [&](auto refill_tag, int rg) -> f32x4 {
+        constexpr bool REFILL = decltype(refill_tag)::value;
+        vm_wait1(wsc, std::integral_constant<int, MT>{});
+        sstage[wave][lane] = wsc;
+        asm volatile("" ::: "memory");
+        if constexpr (REFILL)
+            wsc = buffer_load_b128_nt(srsrc, scale_off(rg - rg0 + 1));
+        const char *sbase = reinterpret_cast<const char *>(&sstage[wave][0]) + i * 8;
         f32x4 acc = zero, p1 = zero, p2 = zero;
         float s1 = 0.f, s2 = 0.f;
+        static_for<MT>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            // E4M3 scales of blocks 0..7 of tile t for weight row i.
+            const u32x2 sb = *reinterpret_cast<const u32x2 *>(sbase + t * 128);
+            float sc[kBlocksPerTile];
+            static_for<4>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sb[h >> 1], (h & 1) != 0);
+                sc[2 * h] = f2[0];
+                sc[2 * h + 1] = f2[1];
+            });
+            vm_wait1(wc[t], std::integral_constant<int, REFILL ? MT : MT - 1 - t>{});
+            const u32x4 c = wc[t];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            {
-                // Every slot has 2*PFD*MT - 1 loads issued after its codes
-                // and 2*PFD*MT - 2 after its scales (stores of Y issued in
-                // between only make the wait stricter).
-                vm_wait2(wc[D][t], ws[D][t], std::integral_constant<int, 2 * PFD * MT - 2>{});
-                const u32x4 c = wc[D][t];
-                const u32x2 s = ws[D][t];
+            for (int b = 0; b < kBlocksPerTile; ++b) {
+                // B operand: W[row i][16*block + 4*g + e], e = 0..3, from
+                // bytes 2*(b&1) and 2*(b&1)+1 of dword b/2.
+                const u32 cw = c[b >> 1];
+                const u32 lo = fp4x2_to_bf16x2(cw, (b & 1) * 2);
+                const u32 hi = fp4x2_to_bf16x2(cw, (b & 1) * 2 + 1);
+                const s16x4 bop = __builtin_bit_cast(s16x4, u32x2{lo, hi});
+                const s16x4 aop = __builtin_bit_cast(s16x4, xr[t][b]);
+                const f32x4 pr = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, zero, 0, 0, 0);
 #pragma unroll
-                for (int b = 0; b < kBlocksPerTile; ++b) {
-                    // B operand: W[row i][16*block + 4*g + e], e = 0..3, from
-                    // bytes 2*(b&1) and 2*(b&1)+1 of dword b/2.
-                    const u32 cw = c[b >> 1];
-                    const u32 lo = fp4x2_to_bf16x2(cw, (b & 1) * 2);
-                    const u32 hi = fp4x2_to_bf16x2(cw, (b & 1) * 2 + 1);
-                    const s16x4 bop = __builtin_bit_cast(s16x4, u32x2{lo, hi});
-                    const s16x4 aop = __builtin_bit_cast(s16x4, xr[t][b]);
-                    const f32x4 pr = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, zero, 0, 0, 0);
-                    const float sc = fp8_to_f32(s[b >> 2], b & 3);
-                    acc[0] = __builtin_fmaf(s2, p2[0], acc[0]);
-                    acc[1] = __builtin_fmaf(s2, p2[1], acc[1]);
-                    acc[2] = __builtin_fmaf(s2, p2[2], acc[2]);
-                    acc[3] = __builtin_fmaf(s2, p2[3], acc[3]);
-                    p2 = p1;
-                    s2 = s1;
-                    p1 = pr;
-                    s1 = sc;
-                    // Pin the FMAs of this step here (instruction selection
-                    // would otherwise sink the whole FMA chain below every
-                    // MFMA and keep all partials live).
-                    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-                }
-                // Refill the slot once its codes and scales are consumed, so
-                // the next tile lands in the same registers.  The scheduling
-                // barrier keeps later tiles' work (and so their waits on
-                // loads still in flight) below this point.
-                load_tile(rg - rg0 + PFD, t, wc[D][t], ws[D][t]);
+                for (int v = 0; v < NV; ++v)
+                    acc[v] = __builtin_fmaf(s2, p2[v], acc[v]);
+                p2 = p1;
+                s2 = s1;
+                p1 = pr;
+                s1 = sc[b];
+                // Pin the FMAs of this step here (instruction selection
+                // would otherwise sink the whole FMA chain below every
+                // MFMA and keep all partials live).
+                asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
             }
-        }
+            // Refill the slot once its codes are consumed, so the next
+            // row group's tile lands in the same registers.
+            if constexpr (REFILL)
+                wc[t] = buffer_load_b128_nt(crsrc, code_off(rg - rg0 + 1, t));
+        });
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < NV; ++v)
             acc[v] = __builtin_fmaf(s1, p1[v], __builtin_fmaf(s2, p2[v], acc[v]));
         return acc;
     };
 
     // Sum the K-slices of row group rg in wave order 0..W-1, scale by gscale,
-    // round to bf16 and store the row group's outputs.
+    // round to bf16 and store the row group's outputs.  Component v of lane
+    // (g, i) is token 4v + g of weight row 16*rg + i.
     auto reduce_store = [&](int rg, int slot) {
         f32x4 sum = part[slot][0][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) {
             const f32x4 q = part[slot][w][lane];
-            sum[0] = sum[0] + q[0];
-            sum[1] = sum[1] + q[1];
-            sum[2] = sum[2] + q[2];
-            sum[3] = sum[3] + q[3];
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                sum[v] = sum[v] + q[v];
         }
         const int r = rg * kRowsPerGroup + i;
         if (r < p.N) {
@@ -337,8 +332,8 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
             else
                 off = p.off0 + r;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int tok = 4 * g + v;
+            for (int v = 0; v < NV; ++v) {
+                const int tok = 4 * v + g;
                 if (tok < p.n)
                     p.Y[(long long)tok * p.ldy + off] = f32_to_bf16_bits(p.gscale * sum[v]);
             }
@@ -360,28 +355,9 @@ __global__ __launch_bounds__(W * 64) void nvfp4_gemv_kernel(GemvParams p)
         }
     };
 
-    // With two ring sets the loop always runs both halves (past the last row
-    // group the ring holds zeros from out-of-range loads and the result is
-    // dropped), so the loop has a single exit and every wait count is exact.
-    for (int rg = rg0; rg < rg1; rg += PFD) {
-        finish(rg, rowgroup(std::integral_constant<int, 0>{}, rg));
-        if constexpr (PFD == 2) {
-            const f32x4 acc = rowgroup(std::integral_constant<int, 1>{}, rg + 1);
-            if (rg + 1 < rg1)
-                finish(rg + 1, acc);
-        }
-    }
-
-    // The last round's refills (zeros from past the end) are never read, but
-    // the hardware still writes their registers when they return.  Wait for
-    // them with the ring registers tied, so the compiler cannot hand those
-    // registers to other values while the loads are in flight.
-    static_for<PFD>([&](auto dc) {
-        static_for<MT>([&](auto tc) {
-            vm_wait2(wc[decltype(dc)::value][decltype(tc)::value], ws[decltype(dc)::value][decltype(tc)::value],
-                     std::integral_constant<int, 0>{});
-        });
-    });
+    for (int rg = rg0; rg < rg1 - 1; ++rg)
+        finish(rg, rowgroup(std::true_type{}, rg));
+    finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1));
 }
 
 // ---- pack: canonical -> tiled device layout --------------------------------
@@ -540,48 +516,40 @@ __global__ void nvfp4_quantize_kernel(const float4 *W, long long nblocks, uint2 
 
 typedef void (*GemvKernel)(GemvParams);
 
-template <int W, int MT, int PFD>
+template <int MT, int NV>
 GemvKernel pick_exact(bool exact)
 {
-    if constexpr (PFD == 2 && MT > 6)
-        return nullptr;   // two row groups of 7-8 tiles do not fit the VGPR budget
-    else
-        return exact ? nvfp4_gemv_kernel<W, MT, PFD, true> : nvfp4_gemv_kernel<W, MT, PFD, false>;
+    return exact ? nvfp4_gemv_kernel<MT, NV, true> : nvfp4_gemv_kernel<MT, NV, false>;
 }
 
-template <int W, int PFD>
+template <int NV>
 GemvKernel pick_mt(int mt, bool exact)
 {
     switch (mt) {
-    case 1: return pick_exact<W, 1, PFD>(exact);
-    case 2: return pick_exact<W, 2, PFD>(exact);
-    case 3: return pick_exact<W, 3, PFD>(exact);
-    case 4: return pick_exact<W, 4, PFD>(exact);
-    case 5: return pick_exact<W, 5, PFD>(exact);
-    case 6: return pick_exact<W, 6, PFD>(exact);
-    case 7: return pick_exact<W, 7, PFD>(exact);
-    default: return pick_exact<W, 8, PFD>(exact);
+    case 1: return pick_exact<1, NV>(exact);
+    case 2: return pick_exact<2, NV>(exact);
+    case 3: return pick_exact<3, NV>(exact);
+    case 4: return pick_exact<4, NV>(exact);
+    case 5: return pick_exact<5, NV>(exact);
+    case 6: return pick_exact<6, NV>(exact);
+    case 7: return pick_exact<7, NV>(exact);
+    default: return pick_exact<8, NV>(exact);
     }
 }
 
-template <int PFD>
-GemvKernel pick_w(int waves, int mt, bool exact)
+// Kernel for n tokens (ceil(n/4) accumulator components) and MT tiles per wave.
+GemvKernel pick_kernel(int n, int mt, bool exact)
 {
-    switch (waves) {
-    case 1: return pick_mt<1, PFD>(mt, exact);
-    case 2: return pick_mt<2, PFD>(mt, exact);
-    case 4: return pick_mt<4, PFD>(mt, exact);
-    default: return pick_mt<8, PFD>(mt, exact);
+    switch ((n + 3) / 4) {
+    case 1: return pick_mt<1>(mt, exact);
+    case 2: return pick_mt<2>(mt, exact);
+    case 3: return pick_mt<3>(mt, exact);
+    default: return pick_mt<4>(mt, exact);
     }
-}
-
-GemvKernel pick_kernel(int waves, int mt, int pfd, bool exact)
-{
-    return pfd == 2 ? pick_w<2>(waves, mt, exact) : pick_w<1>(waves, mt, exact);
 }
 
 struct Geometry {
-    int workgroups, waves, mt, pfd;
+    int workgroups, mt;
     bool exact;
 };
 
@@ -610,30 +578,21 @@ int current_device_info(int *cus)
     return NVFP4_OK;
 }
 
+// Launch shape for an N x K weight on `cus` compute units: 8 waves per
+// workgroup splitting the K tiles evenly (MT each, the last waves possibly
+// short), one workgroup per compute unit per round, and as few workgroups as
+// keep the number of rounds (row groups per workgroup) at its minimum, so that
+// every workgroup streams the same number of row groups where N allows it.
 bool geometry_for(int N, int K, int cus, Geometry *geo)
 {
     const int T = (K + kTileK - 1) / kTileK;
-    const int RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    geo->exact = false;
-    geo->waves = 0;
-    for (int w = kMaxWaves; w >= 1 && K % kTileK == 0; w >>= 1) {
-        if (T % w == 0 && T / w <= kMaxTilesPerWave) {
-            geo->waves = w;
-            geo->mt = T / w;
-            geo->exact = true;
-            break;
-        }
-    }
-    if (!geo->exact) {
-        if ((T + kMaxWaves - 1) / kMaxWaves > kMaxTilesPerWave)
-            return false;
-        geo->waves = kMaxWaves;
-        geo->mt = (T + kMaxWaves - 1) / kMaxWaves;
-    }
-    geo->pfd = 1;   // measured: a second row group in flight is slower at every decode shape
-    const int per_cu = geo->waves >= 8 ? 1 : 8 / geo->waves;
-    long long wg = (long long)cus * per_cu;
-    geo->workgroups = (int)(RG < wg ? RG : wg);
+    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    geo->mt = (T + kWaves - 1) / kWaves;
+    if (geo->mt > kMaxTilesPerWave)
+        return false;
+    geo->exact = K % kTileK == 0 && T == kWaves * geo->mt;
+    const long long rounds = (RG + cus - 1) / cus;
+    geo->workgroups = (int)((RG + rounds - 1) / rounds);
     return true;
 }
 
@@ -652,7 +611,7 @@ int validate_common(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X,
     if (K % 16 != 0)
         return NVFP4_ERR_SHAPE;
     const int T = (K + kTileK - 1) / kTileK;
-    if ((T + kMaxWaves - 1) / kMaxWaves > kMaxTilesPerWave)
+    if ((T + kWaves - 1) / kWaves > kMaxTilesPerWave)
         return NVFP4_ERR_SHAPE;   // K > 8192: the X slice would not fit in VGPRs
     if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 16) || !aligned(Y, 2))
         return NVFP4_ERR_ALIGN;
@@ -668,13 +627,13 @@ int launch_gemv(const GemvParams &p, hipStream_t stream)
     Geometry geo;
     if (!geometry_for(p.N, p.K, cus, &geo))
         return NVFP4_ERR_SHAPE;
-    GemvKernel k = pick_kernel(geo.waves, geo.mt, geo.pfd, geo.exact);
-    if (!k)
-        return NVFP4_ERR_SHAPE;
+    GemvKernel k = pick_kernel(p.n, geo.mt, geo.exact);
     GemvParams q = p;
     q.rg_base = p.RG / geo.workgroups;
     q.rg_rem = p.RG % geo.workgroups;
-    hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(geo.waves * 64), 0, stream, q);
+    if ((long long)(q.rg_base + 1) * p.T * 1024 > 0x7FFFFFFFLL)
+        return NVFP4_ERR_SHAPE;   // a workgroup's codes must stay within a 32-bit buffer offset
+    hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(kWaves * 64), 0, stream, q);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
@@ -899,7 +858,7 @@ int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves, int 
     if (!geometry_for(N, K, cus, &geo))
         return NVFP4_ERR_SHAPE;
     *workgroups = geo.workgroups;
-    *waves = geo.waves;
+    *waves = kWaves;
     *tiles_per_wave = geo.mt;
     return NVFP4_OK;
 }

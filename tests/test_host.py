@@ -50,9 +50,11 @@ def test_dispatcher_schedule_reads_weights_once():
 
 
 def test_launch_geometry_fills_the_chip():
-    assert nv.launch_geometry(16, 16384, 5120) == (256, 8, 5)
-    assert nv.launch_geometry(1, 14336, 5120) == (256, 8, 5)
-    assert nv.launch_geometry(16, 5120, 6144) == (256, 8, 6)
+    # one workgroup per compute unit per round, ranges as even as N allows:
+    # every workgroup streams the same number of 16-row groups
+    assert nv.launch_geometry(16, 16384, 5120) == (256, 8, 5)    # 1024 row groups: 4 each
+    assert nv.launch_geometry(1, 14336, 5120) == (224, 8, 5)     # 896 row groups: 4 each
+    assert nv.launch_geometry(16, 5120, 6144) == (160, 8, 6)     # 320 row groups: 2 each
     assert nv.launch_geometry(1, 1024, 1024) == (64, 8, 1)
     wg, waves, tpw = nv.launch_geometry(1, 37, 144)     # ragged: 3 row groups, 2 tiles
     assert wg == 3 and waves * tpw >= 2
