@@ -1,22 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 decode projection on one MI355X.
 
-Workload (default): the fused attention QKV projection, W 14336 x 5120 NVFP4
-(q|k|v = 8192|3072|3072 rows, written straight to per-projection offsets),
-x bf16 N(0,1), n = 16 decode tokens per step.  A step is one projection of
-the whole token batch (one nvfp4_gemv_qkv call).  Weights are synthetic
-(N(0, 0.02) fp32 quantised on the GPU with the library's quantiser), one
-distinct copy per rotation slot, with enough copies (>= 1 GiB) that the 256 MB
-Infinity Cache cannot serve them: every call reads its weight from HBM.
+Headline workload (the metric line): the fused attention QKV projection,
+W 14336 x 5120 NVFP4 (q|k|v = 8192|3072|3072 rows, written straight to
+per-projection offsets), x bf16 N(0,1), n = 16 decode tokens per step.  A step
+is one projection of the whole token batch (one nvfp4_gemv_qkv call).  Weights
+are synthetic (N(0, 0.02) fp32 quantised on the GPU with the library's
+quantiser), one distinct copy per rotation slot, with enough copies (>= 1 GiB)
+that the 256 MB Infinity Cache cannot serve them: every call reads its weight
+from HBM.
 
-Timing: W warm-up steps, then exactly K steps replayed from a HIP graph
-(launches back-to-back on one stream, no host launch overhead) between two
-device synchronisations, timed with HIP events on that stream.
+Timing: after building the weights, the timed graph is replayed untimed for
+a settle period (the quantiser's fp64 kernels leave the GPU below its steady
+clock for ~10 ms), then W warm-up steps, then exactly K steps replayed from a
+HIP graph (launches back-to-back on one stream, no host launch overhead)
+between two device synchronisations, timed with HIP events on that stream.
 
-Printed: one JSON line with the headline metric (effective weight GB/s =
-N*K*9/16 bytes per call / time per call), GEMV-tokens/s, a per-n sweep
-(n = 1, 2, 3, 4, 8, 16), the roofline of the GEMV kernel and the CPU oracle's
-rate on a bounded sample of the same workload.
+Also measured (default; --quick skips them):
+  * per-n sweep n = 1..16 of every decode shape (fused QKV through both entry
+    points, ssm_qkvz with per-token row scales, ssm_out_proj), cold and warm;
+  * token-tile schedules on ssm_qkvz: the pages' greedy 3-token tiling
+    against one launch for all tokens, for every n;
+  * ssm_out_proj with 1% all-zero blocks and 1% 50x-rms outliers;
+  * the decode-step sweep: 48 distinct ssm_qkvz + 16 distinct fused-QKV
+    matrices (2.93 GB) back to back on one stream at n = 16;
+  * the achievable read ceiling of each shape (nvfp4_read_stream over the
+    same bytes, same rotation) and the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -38,7 +47,9 @@ SHAPES = {
     "smoke_1024x1024": (1024, 1024),
 }
 QKV_ROWS = (8192, 3072, 3072)
+QKV_OFFS = (0, 8192, 11264)
 ROTATION_BYTES = 1 << 30
+SETTLE_S = 0.03
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_n16_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_02_amd", "csrc", "nvfp4.hip")
 
@@ -52,28 +63,53 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class Rotation:
-    """Distinct packed copies of one weight shape, totalling >= ROTATION_BYTES."""
+def zero_outlier_(torch, W, gen, frac=0.01, factor=50.0):
+    """In place on a [N, K] fp32 device tensor: two disjoint random 1% sets of
+    16-element K-blocks; the first set becomes all zero, in the second one
+    uniformly chosen element becomes sign(orig) * factor * rms(orig block)."""
+    N, K = W.shape
+    Wb = W.view(N * (K // 16), 16)
+    nb = Wb.shape[0]
+    perm = torch.randperm(nb, generator=gen, device=W.device)
+    nz = no = int(round(frac * nb))
+    zb, ob = perm[:nz], perm[nz:nz + no]
+    pos = torch.randint(0, 16, (no,), generator=gen, device=W.device)
+    rms = Wb[ob].double().pow(2).mean(dim=1).sqrt()
+    orig = Wb[ob, pos]
+    sign = torch.where(orig < 0, -1.0, 1.0).double()
+    Wb[zb] = 0.0
+    Wb[ob, pos] = (sign * factor * rms).float()
+    return W
 
-    def __init__(self, nv, torch, N, K, seed, min_bytes=ROTATION_BYTES):
+
+class Rotation:
+    """Distinct packed copies of one weight shape, totalling >= min_bytes."""
+
+    def __init__(self, nv, torch, N, K, seed, min_bytes=ROTATION_BYTES, count=None,
+                 zero_outlier=False):
         from nvfp4_weight_only_02_amd import metrics
         self.N, self.K = N, K
         wb = metrics.weight_bytes(N, K)
-        self.count = max(2, math.ceil(min_bytes / wb))
+        self.count = count or max(2, math.ceil(min_bytes / wb))
         self.copies = []
         gen = torch.Generator(device="cuda")
         for c in range(self.count):
             gen.manual_seed(seed + c)
             W = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+            if zero_outlier:
+                zero_outlier_(torch, W, gen)
             self.copies.append(nv.PackedWeight.from_float(W))
             del W
         torch.cuda.synchronize()
 
 
-def make_x(torch, n, K, seed):
+def make_x(torch, n, K, seed, row_scale=False):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
-    return torch.randn((n, K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    x = torch.randn((n, K), generator=gen, device="cuda", dtype=torch.float32)
+    if row_scale:   # per-token row scale U(0.5, 2)
+        x = x * (0.5 + 1.5 * torch.rand((n, 1), generator=gen, device="cuda", dtype=torch.float32))
+    return x.to(torch.bfloat16)
 
 
 _hip = None
@@ -105,6 +141,14 @@ def capture(torch, fn, launches):
     return g
 
 
+def settle(torch, g, seconds=SETTLE_S):
+    """Untimed replays until `seconds` of wall time have passed."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        torch.cuda.synchronize()
+
+
 def copy_calibration(torch, mib=256, reps=5):
     """A plain device copy of known size (for scaling the FETCH_SIZE and
     WRITE_SIZE counters): each copy reads and writes exactly `mib` MiB."""
@@ -132,33 +176,103 @@ def time_graph(torch, g, replays):
     return e0.elapsed_time(e1) * 1e-3
 
 
-def sweep_shape(nv, torch, metrics, rot, n_list, call, launches_per_graph, replays):
-    out = {}
+def time_calls(torch, call, count, replays=4):
+    """Seconds per call of call(i) for i cycling over `count` rotation slots:
+    a graph of 2*count launches, one untimed replay, then `replays` timed."""
+    L = 2 * count
+    g = capture(torch, call, L)
+    g.replay()
+    t = time_graph(torch, g, replays) / (L * replays)
+    del g
+    return t
+
+
+def point(t, wb, n, t1=None, warm=None):
+    from nvfp4_weight_only_02_amd import metrics
+    r = {"us": round(t * 1e6, 3),
+         "weight_GBps": round(wb / t / 1e9, 1),
+         "frac_hbm_peak": round(wb / t / 1e9 / metrics.HBM_PEAK_GBPS, 4),
+         "gemv_tokens_per_s": round(n / t, 1)}
+    if t1:
+        r["t_over_t1"] = round(t / t1, 3)
+    if warm is not None:
+        r["warm_us"] = round(warm * 1e6, 3)
+    return r
+
+
+def sweep_shape(torch, rot, n_list, call, x_seed, row_scale=False, warm=True):
+    """Cold (rotation) and warm (same copy) time per call for each n."""
+    from nvfp4_weight_only_02_amd import metrics
     wb = metrics.weight_bytes(rot.N, rot.K)
+    Xs = make_x(torch, 16, rot.K, x_seed)
+    Ys = torch.empty((16, rot.N), dtype=torch.bfloat16, device="cuda")
+    gs = capture(torch, lambda i: call(rot.copies[i % rot.count], Xs, Ys), rot.count)
+    settle(torch, gs)
+    del gs
+    out, t1 = {}, None
     for n in n_list:
-        X = make_x(torch, n, rot.K, 2000 + n)
+        X = make_x(torch, n, rot.K, x_seed + n, row_scale)
         Y = torch.empty((n, rot.N), dtype=torch.bfloat16, device="cuda")
-        g = capture(torch, lambda i: call(rot.copies[i % rot.count], X, Y), launches_per_graph)
-        g.replay()
-        t = time_graph(torch, g, replays) / (launches_per_graph * replays)
-        # warm reference: the same weight copy on every call (served by the caches)
-        gw = capture(torch, lambda i: call(rot.copies[0], X, Y), 32)
-        gw.replay()
-        tw = time_graph(torch, gw, 4) / 128
-        out[str(n)] = {
-            "us": round(t * 1e6, 3),
-            "weight_GBps": round(wb / t / 1e9, 1),
-            "frac_hbm_peak": round(wb / t / 1e9 / metrics.HBM_PEAK_GBPS, 4),
-            "gemv_tokens_per_s": round(n / t, 1),
-            "t_over_t1": None,
-            "warm_us": round(tw * 1e6, 3),
-        }
-        del g, gw
-    t1 = out[str(n_list[0])]["us"] if n_list[0] == 1 else None
-    for n in n_list:
-        if t1:
-            out[str(n)]["t_over_t1"] = round(out[str(n)]["us"] / t1, 3)
+        t = time_calls(torch, lambda i: call(rot.copies[i % rot.count], X, Y), rot.count)
+        tw = time_calls(torch, lambda i: call(rot.copies[0], X, Y), 32) if warm else None
+        if n == 1:
+            t1 = t
+        out[str(n)] = point(t, wb, n, t1, tw)
     return out
+
+
+def read_ceiling(nv, torch, N, K):
+    """Seconds per read of one weight's bytes with nvfp4_read_stream, over a
+    >= 1 GiB rotation of distinct buffers (the same cold regime)."""
+    from nvfp4_weight_only_02_amd import metrics
+    wb = metrics.weight_bytes(N, K)
+    count = max(2, math.ceil(ROTATION_BYTES / wb))
+    bufs = [torch.full((wb,), c & 0xFF, dtype=torch.uint8, device="cuda") for c in range(count)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t = time_calls(torch, lambda i: nv.read_stream(bufs[i % count], sink), count, replays=6)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"us": round(t * 1e6, 3), "GBps": round(wb / t / 1e9, 1),
+            "frac_hbm_peak": round(wb / t / 1e9 / metrics.HBM_PEAK_GBPS, 4)}
+
+
+def decode_step(nv, torch, n=16):
+    """48 distinct ssm_qkvz + 16 distinct fused-QKV matrices in the layer
+    order of a 64-layer hybrid model (every 4th layer full attention), one
+    projection each per decode step, back to back on one stream."""
+    from nvfp4_weight_only_02_amd import metrics
+    Nz, Kz = SHAPES["ssm_qkvz_16384x5120"]
+    Nq, Kq = SHAPES["fused_qkv_14336x5120"]
+    rz = Rotation(nv, torch, Nz, Kz, seed=5100, count=48)
+    rq = Rotation(nv, torch, Nq, Kq, seed=6100, count=16)
+    X = make_x(torch, n, Kz, 2300 + n)
+    Yz = torch.empty((n, Nz), dtype=torch.bfloat16, device="cuda")
+    Yq = torch.empty((n, Nq), dtype=torch.bfloat16, device="cuda")
+    order = []
+    for layer in range(64):
+        if layer % 4 == 3:
+            order.append(("q", len([o for o in order if o[0] == "q"])))
+        else:
+            order.append(("z", len([o for o in order if o[0] == "z"])))
+
+    def call(i):
+        kind, j = order[i]
+        if kind == "q":
+            nv.gemv_qkv(rq.copies[j], X, QKV_ROWS, QKV_OFFS, Nq, out=Yq)
+        else:
+            nv.gemv(rz.copies[j], X, out=Yz)
+    g = capture(torch, call, 64)
+    settle(torch, g)
+    t = time_graph(torch, g, 20) / 20
+    total = 48 * metrics.weight_bytes(Nz, Kz) + 16 * metrics.weight_bytes(Nq, Kq)
+    del g, rz, rq
+    torch.cuda.empty_cache()
+    return {"n": n, "matrices": "48 ssm_qkvz 16384x5120 + 16 fused QKV 14336x5120",
+            "weight_bytes": total, "us_per_step": round(t * 1e6, 2),
+            "weight_GBps": round(total / t / 1e9, 1),
+            "frac_hbm_peak": round(total / t / 1e9 / metrics.HBM_PEAK_GBPS, 4),
+            "timing": "20 replays of a HIP graph of the 64 launches of one step"}
 
 
 def cpu_baseline(N, K, n, seconds):
@@ -191,7 +305,7 @@ def cpu_baseline(N, K, n, seconds):
     }
 
 
-def stored_traffic(launch_bytes):
+def stored_traffic():
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None if the summary is absent or was taken on a different kernel."""
     try:
@@ -211,8 +325,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--n", type=int, default=16)
     ap.add_argument("--workload", default="fused_qkv_14336x5120", choices=sorted(SHAPES))
-    ap.add_argument("--sweep", default="1,2,3,4,8,16", help="token counts of the per-n sweep ('' = none)")
-    ap.add_argument("--all-shapes", action="store_true", help="also sweep ssm_qkvz, ssm_out_proj and the decode-step set")
+    ap.add_argument("--sweep", default=",".join(str(v) for v in range(1, 17)),
+                    help="token counts of the per-n sweeps ('' = none)")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline and its per-n sweep only (no other shapes, schedules, decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
@@ -246,10 +362,8 @@ def main():
     log("rotation: %d copies, %.2f GiB" % (rot.count, rot.count * metrics.weight_bytes(N, K) / 2**30))
 
     if qkv:
-        offs = (0, QKV_ROWS[0], QKV_ROWS[0] + QKV_ROWS[1])
-
         def call(w, X, Y):
-            nv.gemv_qkv(w, X, QKV_ROWS, offs, N, out=Y)
+            nv.gemv_qkv(w, X, QKV_ROWS, QKV_OFFS, N, out=Y)
     else:
         def call(w, X, Y):
             nv.gemv(w, X, out=Y)
@@ -260,8 +374,8 @@ def main():
     # largest divisor of K up to 64; very long graphs add per-node overhead).
     L = max(d for d in range(1, min(args.steps, 64) + 1) if args.steps % d == 0)
     gt = capture(torch, lambda i: call(rot.copies[i % rot.count], X, Y), L)
-    # Warm-up: W steps, as whole replays of the timed graph itself (its first
-    # replay costs more than the others) plus a remainder graph.
+    settle(torch, gt)
+    # Warm-up: W steps, as whole replays of the timed graph plus a remainder graph.
     if args.warmup % L:
         gw = capture(torch, lambda i: call(rot.copies[i % rot.count], X, Y), args.warmup % L)
         gw.replay()
@@ -301,7 +415,7 @@ def main():
         "config": {"workload": args.workload, "N": N, "K": K, "n_tokens": n,
                    "qkv_rows": list(QKV_ROWS) if qkv else None,
                    "launch": {"workgroups": wg, "waves_per_workgroup": waves, "tiles_per_wave": tpw},
-                   "timing": "%d replays of a HIP graph of %d back-to-back launches, HIP events on the launch stream" % (args.steps // L, L)},
+                   "timing": "%d replays of a HIP graph of %d back-to-back launches, HIP events on the launch stream, after %.0f ms of untimed settle replays and %d warm-up steps" % (args.steps // L, L, SETTLE_S * 1e3, args.warmup)},
         "frac_hbm_peak": round(value / metrics.HBM_PEAK_GBPS, 4),
         "gemv_tokens_per_s": round(n / t_call, 1),
         "host_wall_s_timed_region": round(t_host, 6),
@@ -311,41 +425,78 @@ def main():
             "peak": metrics.HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ab / t_call / 1e9 / metrics.HBM_PEAK_GBPS, 4),
-            "traffic": stored_traffic(ab),
-            "kernel": "nvfp4_gemv_kernel<%d,%d,%s>" % (waves, tpw, "true" if K % 128 == 0 else "false"),
+            "traffic": stored_traffic(),
+            "kernel": "nvfp4_gemv_kernel<%d,%d,%s>" % (tpw, (n + 3) // 4, "true" if K % 128 == 0 else "false"),
             "algorithmic_bytes_per_launch": ab,
         },
     }
+    del gt
+    if args.profile_only:
+        print(json.dumps(result), flush=True)
+        return
 
-    if not args.profile_only:
-        n_list = [int(v) for v in args.sweep.split(",") if v.strip()]
+    n_list = [int(v) for v in args.sweep.split(",") if v.strip()]
+    sweeps = {}
+    if n_list:
+        log("per-n sweep %s ..." % args.workload)
+        sweeps[args.workload] = sweep_shape(torch, rot, n_list, call, 2000)
+        if qkv:
+            sweeps[args.workload + " (plain nvfp4_gemv)"] = sweep_shape(
+                torch, rot, n_list, lambda w, X, Y: nv.gemv(w, X, out=Y), 2000, warm=False)
+    ceil = {args.workload: read_ceiling(nv, torch, N, K)}
+    result["read_ceiling"] = ceil
+    result["frac_read_ceiling"] = round(ceil[args.workload]["us"] * 1e-6 / t_call, 4)
+    del rot
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        plain = lambda w, X, Y: nv.gemv(w, X, out=Y)
+        Nz, Kz = SHAPES["ssm_qkvz_16384x5120"]
+        log("ssm_qkvz: sweep and schedules ...")
+        rz = Rotation(nv, torch, Nz, Kz, seed=3100)
         if n_list:
-            log("per-n sweep ...")
-            result["sweep"] = {args.workload: sweep_shape(nv, torch, metrics, rot, n_list, call,
-                                                          2 * rot.count, 4)}
-            # warm-cache reference: the same weight copy every call
-            Xw = make_x(torch, n, K, 77)
-            Yw = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
-            gww = capture(torch, lambda i: call(rot.copies[0], Xw, Yw), 64)
-            gww.replay()
-            tw = time_graph(torch, gww, 4) / 256
-            result["warm_same_weight"] = {"n": n, "us": round(tw * 1e6, 3),
-                                          "weight_GBps": round(wb / tw / 1e9, 1)}
-        if args.all_shapes:
-            del rot, gt
-            torch.cuda.empty_cache()
-            for name in ("ssm_qkvz_16384x5120", "ssm_out_proj_5120x6144"):
-                log("sweep", name)
-                N2, K2 = SHAPES[name]
-                r2 = Rotation(nv, torch, N2, K2, seed=3100)
-                result["sweep"][name] = sweep_shape(
-                    nv, torch, metrics, r2, n_list or [1, 16],
-                    lambda w, X, Y: nv.gemv(w, X, out=Y), 2 * r2.count, 4)
-                del r2
-                torch.cuda.empty_cache()
-        if not args.no_cpu_baseline:
-            log("cpu baseline ...")
-            result["cpu_baseline"] = cpu_baseline(N, K, n, args.cpu_seconds)
+            sweeps["ssm_qkvz_16384x5120"] = sweep_shape(torch, rz, n_list, plain, 2300, row_scale=True)
+        wbz = metrics.weight_bytes(Nz, Kz)
+        sched = {}
+        for nn in (n_list or [16]):
+            Xs = make_x(torch, nn, Kz, 2300 + nn, row_scale=True)
+            Ys = torch.empty((nn, Nz), dtype=torch.bfloat16, device="cuda")
+            greedy = nv.schedule_greedy(nn, 3)
+            row = {"greedy_3": greedy,
+                   "greedy_us": round(time_calls(torch, lambda i: nv.gemv_sched(
+                       rz.copies[i % rz.count], Xs, greedy, out=Ys), rz.count) * 1e6, 3),
+                   "one_launch_us": sweeps.get("ssm_qkvz_16384x5120", {}).get(str(nn), {}).get("us")}
+            if nn == 16:
+                for name, w in (("8+8", [8, 8]), ("4x4", [4, 4, 4, 4]), ("16", [16])):
+                    row[name + "_us"] = round(time_calls(torch, lambda i: nv.gemv_sched(
+                        rz.copies[i % rz.count], Xs, w, out=Ys), rz.count) * 1e6, 3)
+            sched[str(nn)] = row
+        result["schedules_ssm_qkvz"] = sched
+        ceil["ssm_qkvz_16384x5120"] = read_ceiling(nv, torch, Nz, Kz)
+        del rz
+        torch.cuda.empty_cache()
+
+        No, Ko = SHAPES["ssm_out_proj_5120x6144"]
+        log("ssm_out_proj: sweep, zero/outlier tensor ...")
+        ro = Rotation(nv, torch, No, Ko, seed=4100)
+        if n_list:
+            sweeps["ssm_out_proj_5120x6144"] = sweep_shape(torch, ro, n_list, plain, 2400)
+        del ro
+        torch.cuda.empty_cache()
+        rzo = Rotation(nv, torch, No, Ko, seed=4600, zero_outlier=True)
+        sweeps["ssm_out_proj_5120x6144 (1% zero + 1% outlier blocks)"] = sweep_shape(
+            torch, rzo, [1, 4, 16], plain, 2400, warm=False)
+        ceil["ssm_out_proj_5120x6144"] = read_ceiling(nv, torch, No, Ko)
+        del rzo
+        torch.cuda.empty_cache()
+
+        log("decode-step sweep ...")
+        result["decode_step"] = decode_step(nv, torch)
+
+    result["sweep"] = sweeps
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        result["cpu_baseline"] = cpu_baseline(N, K, n, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 

@@ -139,6 +139,17 @@ int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles);
 int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves,
                           int *tiles_per_wave);
 
+/* Measurement aid, not part of the GEMV path: reads `bytes` bytes of `buf`
+ * (DEVICE, 16-byte aligned, bytes a positive multiple of 16) once with the
+ * streaming pattern that reads fastest on MI355X (1024-thread workgroups,
+ * contiguous chunks, four 16-byte non-temporal loads in flight per lane) and
+ * writes a checksum of the data to *sink (DEVICE, 4 bytes) so that no load
+ * is dead.  Timing it gives the achievable HBM read ceiling the GEMV's
+ * effective weight bandwidth is compared with (the pages compare their
+ * kernels with a STREAM-measured ceiling in the same way).  Asynchronous on
+ * `stream`; errors: NULL, RANGE (bytes), ALIGN, DEVICE, LAUNCH. */
+int nvfp4_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);
 

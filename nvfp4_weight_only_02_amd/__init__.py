@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_launch_geometry.restype = _i32
         L.nvfp4_launch_geometry.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32),
                                             ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        L.nvfp4_read_stream.restype = _i32
+        L.nvfp4_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.nvfp4_strerror.restype = ctypes.c_char_p
         L.nvfp4_strerror.argtypes = [_i32]
         _lib = L
@@ -227,6 +229,14 @@ def gemv_sched(w: PackedWeight, X: torch.Tensor, tile_widths, out: torch.Tensor 
                                   Y.data_ptr(), n, w.N, w.K, widths, len(tile_widths),
                                   _stream(stream)), "nvfp4_gemv_sched")
     return Y
+
+
+def read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of ``buf`` once (measurement aid for the read ceiling)."""
+    _dev(buf, torch.uint8, "buf")
+    _dev(sink, torch.int32, "sink")
+    _check(lib().nvfp4_read_stream(buf.data_ptr(), buf.numel(), sink.data_ptr(), _stream(stream)),
+           "nvfp4_read_stream")
 
 
 def gemv_qkv(w: PackedWeight, X: torch.Tensor, rows, out_off, ldy: int,

@@ -274,3 +274,16 @@ def test_full_size_parity(name, N, K, cfg, zero_outlier, row_scale, n):
     Y = y_bits(nv.gemv(pw, x_to_dev(X)))
     Yref, Aref = O.gemv(codes, scales, g, X)
     assert_parity(Y, Yref, Aref, "%s n=%d" % (name, n))
+
+
+def test_read_stream_runs_and_leaves_data():
+    """The read-ceiling aid reads a buffer without changing it (sink written
+    only on a checksum value the data below cannot produce)."""
+    say("read_stream 1 MiB + 48 B")
+    buf = torch.arange((1 << 20) + 48, dtype=torch.int32, device="cuda").to(torch.uint8)
+    ref = buf.clone()
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    nv.read_stream(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
+    assert int(sink.item()) == 7

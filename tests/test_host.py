@@ -119,3 +119,12 @@ def test_quantize_and_pack_validation():
     assert L.nvfp4_pack(FAKE, FAKE, 16, 16, FAKE + 8, FAKE, None) == 3
     assert L.nvfp4_pack(FAKE, 0, 16, 16, FAKE, FAKE, None) == 1
     assert L.nvfp4_pack(FAKE, FAKE, 16, 20, FAKE, FAKE, None) == 4
+
+
+def test_read_stream_validation():
+    L = nv.lib()
+    assert L.nvfp4_read_stream(None, 1024, FAKE, None) == 1
+    assert L.nvfp4_read_stream(FAKE, 1024, None, None) == 1
+    assert L.nvfp4_read_stream(FAKE, 0, FAKE, None) == 2
+    assert L.nvfp4_read_stream(FAKE, 1000, FAKE, None) == 2
+    assert L.nvfp4_read_stream(FAKE + 8, 1024, FAKE, None) == 3
