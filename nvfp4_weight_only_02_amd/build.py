@@ -7,6 +7,7 @@ library.  The flags keep hipcc from emitting packed-fp32 VALU instructions
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,15 +37,40 @@ def hipcc() -> str:
     return exe
 
 
+def check_resources(remarks: str) -> None:
+    """Refuse a build in which a GEMV kernel spills registers or uses scratch.
+
+    The GEMV kernels issue their vector-memory loads as inline assembly and
+    wait for them with explicit vmcnt counts; the compiler does not know such
+    a load is still in flight, so a spill (or any other copy) of its
+    destination registers before the wait would read them too early."""
+    kernel = None
+    bad = []
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+            continue
+        if kernel is None or "gemv_kernel" not in kernel:
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) != 0:
+            bad.append("%s: %s = %s" % (kernel, m.group(1), m.group(2)))
+    if bad:
+        raise RuntimeError("GEMV kernels must not spill or use scratch:\n  " + "\n  ".join(bad))
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library (always) and return its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-Rpass-analysis=kernel-resource-usage"] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(line for line in res.stdout.splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    lines = [line for line in res.stdout.splitlines()
+             if "packed-fp32-ops' is not a recognized feature" not in line]
+    check_resources("\n".join(lines))
+    out = "\n".join(line for line in lines if "remark:" not in line)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():

@@ -188,8 +188,9 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // X first (it is cache-resident after the first workgroups touch it, so
     // its staging below never waits for an HBM load): lane (chunk, q) loads
     // the 16-byte chunk `chunk` of token row q*4 + lane/16 of each tile of
-    // the slice (16 lanes cover one row's 256 bytes: whole-line loads).  Load
-    // instructions whose four token rows are all >= n are not issued.
+    // the slice (16 lanes cover one row's 256 bytes: whole-line loads).  Only
+    // the NV = ceil(n/4) load instructions per tile whose four token rows hold
+    // a real token are issued.
     constexpr int kStageRow = kTileK * 2 / 16 + 1;   // 16-byte chunks per row, +1 pad
     __shared__ u32x4 xstage[W][kRowsPerGroup][kStageRow];
     const int chunk = lane & 15;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             xg[t][q] = z4;
-            if (4 * q < p.n) {
+            if (q < NV) {
                 const int row = q * 4 + (lane >> 4);
                 const int k = (tw0 + t) * kTileK + chunk * 8;
                 const bool ok = row < p.n && (EXACT || k < p.K);
@@ -227,18 +228,27 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // Stage X through a per-wave LDS tile into MFMA A-operand layout: lane
     // (i, g) holds X[4*(i%4) + i/4][k .. k+3] with k = 16*block + 4*g, for
     // every block of the slice.  Every X load is older than the MT + 1 ring
-    // loads.
+    // loads.  The staging is LDS-bandwidth bound (all waves of a CU stage at
+    // once), so only the NV token quarters in use are written, and only the
+    // lanes whose MFMA row carries one of them read (the other lanes' A rows
+    // stay zero; they only feed outputs that are never stored).
     u32x2 xr[MT][kBlocksPerTile];
+    const bool xlane = 4 * (i & 3) + (i >> 2) < 4 * NV;
     static_for<MT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, MT + 1>{});
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NV; ++q)
             xstage[wave][q * 4 + (lane >> 4)][chunk] = xg[t][q];
         const char *base = reinterpret_cast<const char *>(&xstage[wave][4 * (i & 3) + (i >> 2)][0]);
 #pragma unroll
         for (int b = 0; b < kBlocksPerTile; ++b)
-            xr[t][b] = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
+            xr[t][b] = u32x2{0u, 0u};
+        if (xlane) {
+#pragma unroll
+            for (int b = 0; b < kBlocksPerTile; ++b)
+                xr[t][b] = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
+        }
     });
 
     // Partial sums of up to kSlots row groups wait in LDS and are reduced

@@ -128,3 +128,22 @@ def test_read_stream_validation():
     assert L.nvfp4_read_stream(FAKE, 0, FAKE, None) == 2
     assert L.nvfp4_read_stream(FAKE, 1000, FAKE, None) == 2
     assert L.nvfp4_read_stream(FAKE + 8, 1024, FAKE, None) == 3
+
+
+def test_build_refuses_spilling_gemv_kernels():
+    """The build check that keeps the GEMV kernels free of spills (their loads
+    are inline assembly waited for by hand; a spill could copy a register
+    whose load is still in flight)."""
+    from nvfp4_weight_only_02_amd import build
+    ok = ("x.hip:1:1: remark: Function Name: _ZN12nvfp4_gemv_kernelILi5E [-Rpass]\n"
+          "x.hip:1:1: remark:     VGPRs: 170 [-Rpass]\n"
+          "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass]\n"
+          "x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass]\n"
+          "x.hip:1:1: remark: Function Name: _ZN12other_kernel [-Rpass]\n"
+          "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 64 [-Rpass]\n")
+    build.check_resources(ok)
+    bad = ok + ("x.hip:1:1: remark: Function Name: _ZN12nvfp4_gemv_kernelILi6E [-Rpass]\n"
+                "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 68 [-Rpass]\n"
+                "x.hip:1:1: remark:     VGPRs Spill: 16 [-Rpass]\n")
+    with pytest.raises(RuntimeError, match="must not spill"):
+        build.check_resources(bad)
