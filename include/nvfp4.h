@@ -91,8 +91,10 @@ int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K,
  * Wq / Wscale: packed layout (nvfp4_pack), 16-byte aligned.
  * X: bf16 [n][K], 16-byte aligned.  Y: bf16 [n][N], 2-byte aligned.
  * Each token's result is bit-identical to the same token computed alone
- * (n = 1) and under any schedule of nvfp4_gemv_sched.
- * Errors: NULL, RANGE, SHAPE (K % 16), ALIGN, LAUNCH, DEVICE. */
+ * (n = 1) and under any schedule of nvfp4_gemv_sched.  Any N >= 1 and any
+ * K % 16 == 0 up to 262144; K beyond 8192 runs in several K-chunk passes
+ * inside the one launch.  Errors: NULL, RANGE, SHAPE (K % 16, K > 262144, or
+ * a workgroup's share of the weight beyond 2 GiB), ALIGN, LAUNCH, DEVICE. */
 int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
                const uint16_t *X, uint16_t *Y, int n, int N, int K, void *stream);
 

@@ -62,10 +62,12 @@ constexpr int kRowsPerGroup = 16;      // MFMA N dimension: weight rows per tile
 constexpr int kTileK = 128;            // K columns per tile (8 NVFP4 blocks)
 constexpr int kBlocksPerTile = kTileK / 16;
 constexpr int kMaxTilesPerWave = 8;    // X slice of a wave: 16 VGPRs per tile
+constexpr int kMaxTilesChunked = 7;    // per wave and K chunk when K needs several chunks
 constexpr int kWaves = 8;            // waves per workgroup, one K-slice each
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer resource: 32-bit data, no swizzle
 constexpr unsigned kOutOfRange = 0x7FFFFFF0u;   // buffer offset past any resource: reads zeros
 constexpr int kSlots = 8;                        // row-group partials parked in LDS
+constexpr int kMaxK = 1 << 18;                   // keeps every buffer offset within 32 bits
 
 struct GemvParams {
     const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
@@ -74,6 +76,7 @@ struct GemvParams {
     uint16_t *Y;           // bf16 output, token stride ldy
     float gscale;
     int n, N, K, T, RG;
+    int kc;                // K chunks (passes): chunk c covers tiles [c*8*MT, (c+1)*8*MT)
     int rg_base, rg_rem;   // row groups per workgroup: rg_base, +1 for the first rg_rem
     int start1, start2;    // first row of the 2nd and 3rd projection (N if absent)
     long long off0, off1, off2, ldy;
@@ -152,11 +155,15 @@ __device__ __forceinline__ void vm_wait1(u32x4 &a, std::integral_constant<int, N
 }
 
 // One launch covers every token (n <= 16) of one weight matrix.
-//   MT    tiles of the K-slice each of the kWaves waves owns;
+//   MT    tiles of the K-slice each of the kWaves waves owns in one K chunk;
 //   NV    ceil(n / 4): accumulator components that carry real tokens;
-//   EXACT every wave owns exactly MT tiles (K == 128 * T, T == kWaves * MT),
-//         so no column predication is needed.
-template <int MT, int NV, bool EXACT>
+//   EXACT every wave owns exactly MT tiles of every chunk (K == 128 * T,
+//         T == kc * kWaves * MT), so no column predication is needed;
+//   CHUNKED K is longer than one chunk (8 waves x 8 tiles, whose X slices
+//         fill the VGPRs): the launch runs kc passes over the workgroup's row
+//         groups, one per K chunk, restaging X for each, and each wave adds
+//         its chunk partials into its own LDS slots in chunk order.
+template <int MT, int NV, bool EXACT, bool CHUNKED>
 __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
 {
     constexpr int W = kWaves;
@@ -168,8 +175,8 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     const int wg = blockIdx.x;
     const int rg0 = wg * p.rg_base + min(wg, p.rg_rem);
     const int rg1 = rg0 + p.rg_base + (wg < p.rg_rem ? 1 : 0);
-    const int tw0 = wave * MT;
-    const int tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+    int tw0 = wave * MT;   // first tile of this wave's slice in the current K chunk
+    int tw = MT;           // tiles of it that exist
 
     // All vector-memory loads of the main path are inline buffer loads waited
     // for with explicit, compile-time vmcnt values: loads retire in issue
@@ -196,18 +203,20 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     const int chunk = lane & 15;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
     u32x4 xg[MT][4];
+    auto issue_x = [&]() {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xg[t][q] = z4;
-            if (q < NV) {
-                const int row = q * 4 + (lane >> 4);
-                const int k = (tw0 + t) * kTileK + chunk * 8;
-                const bool ok = row < p.n && (EXACT || k < p.K);
-                xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
+            for (int q = 0; q < 4; ++q) {
+                xg[t][q] = z4;
+                if (q < NV) {
+                    const int row = q * 4 + (lane >> 4);
+                    const int k = (tw0 + t) * kTileK + chunk * 8;
+                    const bool ok = row < p.n && (EXACT || k < p.K);
+                    xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
+                }
             }
-        }
+    };
 
     // Weight ring: one row group of this wave's K-slice, issued as
     // [scale chunk, code tile 0 .. MT-1].  The scale chunk is the MT * 128
@@ -220,10 +229,12 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     auto code_off = [&](int rgl, int t) -> unsigned {
         return (EXACT || t < tw) ? (unsigned)((rgl * p.T + tw0 + t) * 1024 + lane * 16) : kOutOfRange;
     };
-    wsc = buffer_load_b128_nt(srsrc, scale_off(0));
+    auto issue_ring = [&](int rgl) {
+        wsc = buffer_load_b128_nt(srsrc, scale_off(rgl));
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-        wc[t] = buffer_load_b128_nt(crsrc, code_off(0, t));
+        for (int t = 0; t < MT; ++t)
+            wc[t] = buffer_load_b128_nt(crsrc, code_off(rgl, t));
+    };
 
     // Stage X through a per-wave LDS tile into MFMA A-operand layout: lane
     // (i, g) holds X[4*(i%4) + i/4][k .. k+3] with k = 16*block + 4*g, for
@@ -234,6 +245,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // stay zero; they only feed outputs that are never stored).
     u32x2 xr[MT][kBlocksPerTile];
     const bool xlane = 4 * (i & 3) + (i >> 2) < 4 * NV;
+    auto stage_x = [&]() {
     static_for<MT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, MT + 1>{});
@@ -250,10 +262,12 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 xr[t][b] = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
         }
     });
+    };
 
-    // Partial sums of up to kSlots row groups wait in LDS and are reduced
-    // together, so waves only meet at a barrier once per kSlots row groups
-    // (once per launch at the decode shapes) instead of after every row group.
+    // Partial sums of a batch of up to kSlots row groups wait in LDS (added
+    // up over the K chunks) and are reduced together, so waves only meet at a
+    // barrier once per batch (once per launch at the decode shapes) instead
+    // of after every row group.
     __shared__ f32x4 part[kSlots][W][64];
     __shared__ u32x4 sstage[W][64];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -350,24 +364,60 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         }
     };
 
-    // Park the partial of row group rg; when the slots are full or the last
-    // row group is in, reduce them (slot s by wave s % W) between barriers.
-    auto finish = [&](int rg, const f32x4 acc) {
-        const int slot = (rg - rg0) % kSlots;
-        part[slot][wave][lane] = acc;
-        if (slot == kSlots - 1 || rg == rg1 - 1) {
-            __syncthreads();
-            const int base = rg - slot;
-            for (int sl = wave; sl <= slot; sl += W)
-                reduce_store(base + sl, sl);
-            if (rg != rg1 - 1)
-                __syncthreads();
+    // Add chunk c's partial of the row group in `slot` to this wave's LDS slot.
+    auto park = [&](int slot, int c, const f32x4 acc) {
+        if (c == 0) {
+            part[slot][wave][lane] = acc;
+        } else {
+            f32x4 q = part[slot][wave][lane];
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                q[v] = q[v] + acc[v];
+            part[slot][wave][lane] = q;
         }
     };
 
-    for (int rg = rg0; rg < rg1 - 1; ++rg)
-        finish(rg, rowgroup(std::true_type{}, rg));
-    finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1));
+    // Row groups in batches of up to kSlots (one batch at the decode shapes).
+    auto batch_end = [&](int b0, int b1) {
+        __syncthreads();
+        for (int sl = wave; sl < b1 - b0; sl += W)
+            reduce_store(b0 + sl, sl);
+        if (b1 < rg1)
+            __syncthreads();
+    };
+    if constexpr (CHUNKED) {
+        for (int b0 = rg0; b0 < rg1; b0 += kSlots) {
+            const int b1 = min(b0 + kSlots, rg1);
+            for (int c = 0; c < p.kc; ++c) {
+                tw0 = (c * W + wave) * MT;
+                tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+                issue_x();
+                issue_ring(b0 - rg0);
+                stage_x();
+                for (int rg = b0; rg < b1 - 1; ++rg)
+                    park(rg - b0, c, rowgroup(std::true_type{}, rg));
+                park(b1 - 1 - b0, c, rowgroup(std::false_type{}, b1 - 1));
+            }
+            batch_end(b0, b1);
+        }
+    } else {
+        // One K chunk: X is loaded and staged once for the whole launch, and
+        // the ring runs on across batches (each slot refilled with the next
+        // row group whatever batch it belongs to).
+        tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+        issue_x();
+        issue_ring(0);
+        stage_x();
+        auto finish = [&](int rg, const f32x4 acc) {
+            const int slot = (rg - rg0) % kSlots;
+            park(slot, 0, acc);
+            if (slot == kSlots - 1 || rg == rg1 - 1)
+                batch_end(rg - slot, rg + 1);
+        };
+        for (int rg = rg0; rg < rg1 - 1; ++rg)
+            finish(rg, rowgroup(std::true_type{}, rg));
+        finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1));
+    }
 }
 
 // ---- pack: canonical -> tiled device layout --------------------------------
@@ -557,39 +607,47 @@ __global__ __launch_bounds__(kReadThreads) void nvfp4_read_stream_kernel(const u
 typedef void (*GemvKernel)(GemvParams);
 
 template <int MT, int NV>
-GemvKernel pick_exact(bool exact)
+GemvKernel pick_exact(bool exact, bool chunked)
 {
-    return exact ? nvfp4_gemv_kernel<MT, NV, true> : nvfp4_gemv_kernel<MT, NV, false>;
+    // Several chunks imply more than 64 tiles split into chunks of at most
+    // kMaxTilesChunked tiles per wave, so 5 <= MT <= kMaxTilesChunked.
+    if constexpr (MT >= 5 && MT <= kMaxTilesChunked) {
+        if (chunked)
+            return exact ? nvfp4_gemv_kernel<MT, NV, true, true> : nvfp4_gemv_kernel<MT, NV, false, true>;
+    }
+    if (chunked)
+        return nullptr;
+    return exact ? nvfp4_gemv_kernel<MT, NV, true, false> : nvfp4_gemv_kernel<MT, NV, false, false>;
 }
 
 template <int NV>
-GemvKernel pick_mt(int mt, bool exact)
+GemvKernel pick_mt(int mt, bool exact, bool chunked)
 {
     switch (mt) {
-    case 1: return pick_exact<1, NV>(exact);
-    case 2: return pick_exact<2, NV>(exact);
-    case 3: return pick_exact<3, NV>(exact);
-    case 4: return pick_exact<4, NV>(exact);
-    case 5: return pick_exact<5, NV>(exact);
-    case 6: return pick_exact<6, NV>(exact);
-    case 7: return pick_exact<7, NV>(exact);
-    default: return pick_exact<8, NV>(exact);
+    case 1: return pick_exact<1, NV>(exact, chunked);
+    case 2: return pick_exact<2, NV>(exact, chunked);
+    case 3: return pick_exact<3, NV>(exact, chunked);
+    case 4: return pick_exact<4, NV>(exact, chunked);
+    case 5: return pick_exact<5, NV>(exact, chunked);
+    case 6: return pick_exact<6, NV>(exact, chunked);
+    case 7: return pick_exact<7, NV>(exact, chunked);
+    default: return pick_exact<8, NV>(exact, chunked);
     }
 }
 
 // Kernel for n tokens (ceil(n/4) accumulator components) and MT tiles per wave.
-GemvKernel pick_kernel(int n, int mt, bool exact)
+GemvKernel pick_kernel(int n, int mt, bool exact, bool chunked)
 {
     switch ((n + 3) / 4) {
-    case 1: return pick_mt<1>(mt, exact);
-    case 2: return pick_mt<2>(mt, exact);
-    case 3: return pick_mt<3>(mt, exact);
-    default: return pick_mt<4>(mt, exact);
+    case 1: return pick_mt<1>(mt, exact, chunked);
+    case 2: return pick_mt<2>(mt, exact, chunked);
+    case 3: return pick_mt<3>(mt, exact, chunked);
+    default: return pick_mt<4>(mt, exact, chunked);
     }
 }
 
 struct Geometry {
-    int workgroups, mt;
+    int workgroups, mt, kc;
     bool exact;
 };
 
@@ -627,10 +685,13 @@ bool geometry_for(int N, int K, int cus, Geometry *geo)
 {
     const int T = (K + kTileK - 1) / kTileK;
     const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    geo->mt = (T + kWaves - 1) / kWaves;
-    if (geo->mt > kMaxTilesPerWave)
-        return false;
-    geo->exact = K % kTileK == 0 && T == kWaves * geo->mt;
+    // One chunk up to 8 tiles per wave; beyond, chunks of at most
+    // kMaxTilesChunked tiles per wave (the chunked kernels keep one more
+    // set of X registers live across passes).
+    const int per_chunk = T <= kWaves * kMaxTilesPerWave ? kWaves * kMaxTilesPerWave : kWaves * kMaxTilesChunked;
+    geo->kc = (T + per_chunk - 1) / per_chunk;
+    geo->mt = (T + kWaves * geo->kc - 1) / (kWaves * geo->kc);
+    geo->exact = K % kTileK == 0 && T == geo->kc * kWaves * geo->mt;
     const long long rounds = (RG + cus - 1) / cus;
     geo->workgroups = (int)((RG + rounds - 1) / rounds);
     return true;
@@ -650,9 +711,8 @@ int validate_common(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X,
         return NVFP4_ERR_RANGE;
     if (K % 16 != 0)
         return NVFP4_ERR_SHAPE;
-    const int T = (K + kTileK - 1) / kTileK;
-    if ((T + kWaves - 1) / kWaves > kMaxTilesPerWave)
-        return NVFP4_ERR_SHAPE;   // K > 8192: the X slice would not fit in VGPRs
+    if (K > kMaxK)
+        return NVFP4_ERR_SHAPE;
     if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 16) || !aligned(Y, 2))
         return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
@@ -667,10 +727,13 @@ int launch_gemv(const GemvParams &p, hipStream_t stream)
     Geometry geo;
     if (!geometry_for(p.N, p.K, cus, &geo))
         return NVFP4_ERR_SHAPE;
-    GemvKernel k = pick_kernel(p.n, geo.mt, geo.exact);
+    GemvKernel k = pick_kernel(p.n, geo.mt, geo.exact, geo.kc > 1);
+    if (!k)
+        return NVFP4_ERR_SHAPE;
     GemvParams q = p;
     q.rg_base = p.RG / geo.workgroups;
     q.rg_rem = p.RG % geo.workgroups;
+    q.kc = geo.kc;
     if ((long long)(q.rg_base + 1) * p.T * 1024 > 0x7FFFFFFFLL)
         return NVFP4_ERR_SHAPE;   // a workgroup's codes must stay within a 32-bit buffer offset
     hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(kWaves * 64), 0, stream, q);

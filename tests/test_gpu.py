@@ -117,7 +117,10 @@ def test_gemv_parity_1024(n):
 
 
 @pytest.mark.parametrize("N,K", [(1, 16), (37, 144), (100, 272), (16, 128), (33, 1040),
-                                 (50, 8192), (300, 640), (2049, 96)])
+                                 (50, 8192), (300, 640), (2049, 96),
+                                 # K split into chunks (several X slices per wave):
+                                 # ragged last chunk, exact chunks, ragged K tile
+                                 (40, 8208), (64, 14336), (37, 12304)])
 @pytest.mark.parametrize("n", [1, 5, 16])
 def test_gemv_parity_ragged(N, K, n):
     say("gemv ragged", N, K, n)
@@ -287,3 +290,33 @@ def test_read_stream_runs_and_leaves_data():
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
     assert int(sink.item()) == 7
+
+
+# ---- K longer than one chunk: a dense-FFN down projection -------------------------
+
+@pytest.fixture(scope="module")
+def ffn_down():
+    say("build ffn down 5120x17408")
+    N, K = 5120, 17408
+    W, codes, scales, g = weight_case(N, K, inputs.weight_seed(6))
+    pw = packed_from_canonical(codes, scales, g, N, K)
+    X = inputs.activations_bf16(16, K, inputs.act_seed(6, 16))
+    return pw, codes, scales, g, X
+
+
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_ffn_down_parity(ffn_down, n):
+    say("ffn down parity n", n)
+    pw, codes, scales, g, X = ffn_down
+    Y = y_bits(nv.gemv(pw, x_to_dev(X[:n])))
+    Yref, Aref = O.gemv(codes, scales, g, X[:n])
+    assert_parity(Y, Yref, Aref, "ffn down 5120x17408 n=%d" % n)
+
+
+def test_ffn_down_token_identity(ffn_down):
+    say("ffn down identity across n")
+    pw, _, _, _, X = ffn_down
+    Xd = x_to_dev(X)
+    full = y_bits(nv.gemv(pw, Xd))
+    for n in (1, 3, 8):
+        assert np.array_equal(y_bits(nv.gemv(pw, Xd[:n].contiguous())), full[:n]), n

@@ -77,7 +77,7 @@ FAKE = 0x100000   # 16-byte aligned, never dereferenced: every case below fails 
     ((FAKE, FAKE, 1.0, FAKE, FAKE, 17, 16, 16), 2),      # n > 16
     ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 0, 16), 2),        # N = 0
     ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 24), 4),       # K % 16
-    ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 8192 + 128), 4),  # K beyond the VGPR-resident X slice
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, (1 << 18) + 16), 4),  # K beyond 32-bit buffer offsets
     ((FAKE + 8, FAKE, 1.0, FAKE, FAKE, 1, 16, 16), 3),   # Wq misaligned
     ((FAKE, FAKE, 1.0, FAKE + 2, FAKE, 1, 16, 16), 3),   # X misaligned
     ((FAKE, FAKE, 1.0, FAKE + 8, FAKE, 1, 16, 16), 3),   # X not 16-byte aligned
