@@ -25,7 +25,9 @@ Also measured (default; --quick skips them):
   * the decode-step sweep: 48 distinct ssm_qkvz + 16 distinct fused-QKV
     matrices (2.93 GB) back to back on one stream at n = 16;
   * the achievable read ceiling of each shape (nvfp4_read_stream over the
-    same bytes, same rotation) and the CPU oracle on a bounded sample.
+    same bytes, same rotation) and the CPU oracle on a bounded sample;
+  * shapes beyond the decode projections (dense FFN gate+up and down with
+    K > 8192, the pages' small hidden-2048 attention layer) at n = 1..16.
 """
 from __future__ import annotations
 
@@ -48,6 +50,17 @@ SHAPES = {
 }
 QKV_ROWS = (8192, 3072, 3072)
 QKV_OFFS = (0, 8192, 11264)
+# Shapes beyond the decode projections (name, N, K, fused q|k|v rows or None,
+# what it is).  The FFN intermediate size (17408) is a synthetic choice for a
+# hidden-5120 dense model; the small attention layer is hidden 2048 with 16
+# query heads and 2 KV heads of dimension 256.
+EXTRA_SHAPES = [
+    ("ffn_gate_up_34816x5120", 34816, 5120, None, "dense FFN gate+up fused, intermediate 17408"),
+    ("ffn_down_5120x17408", 5120, 17408, None, "dense FFN down, K in 3 chunk passes"),
+    ("attn_small_qkv_5120x2048", 5120, 2048, (4096, 512, 512), "hidden 2048: fused q|k|v 4096|512|512"),
+    ("attn_small_o_proj_2048x4096", 2048, 4096, None, "hidden 2048: o_proj"),
+]
+EXTRA_N = [1, 2, 4, 8, 16]
 ROTATION_BYTES = 1 << 30
 SETTLE_S = 0.03
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_n16_counters.json")
@@ -492,6 +505,24 @@ def main():
 
         log("decode-step sweep ...")
         result["decode_step"] = decode_step(nv, torch)
+
+        extra = {}
+        for name, Ne, Ke, rows, what in EXTRA_SHAPES:
+            log("extra shape %s ..." % name)
+            re_ = Rotation(nv, torch, Ne, Ke, seed=7100 + Ne % 997)
+            if rows:
+                offs = (0, rows[0], rows[0] + rows[1])
+                ecall = (lambda rws, ofs, ld: lambda w, X, Y: nv.gemv_qkv(w, X, rws, ofs, ld, out=Y))(rows, offs, Ne)
+            else:
+                ecall = plain
+            wg_, wv_, tpw_ = nv.launch_geometry(16, Ne, Ke)
+            extra[name] = {"what": what, "N": Ne, "K": Ke,
+                           "launch": {"workgroups": wg_, "tiles_per_wave": tpw_},
+                           "sweep": sweep_shape(torch, re_, EXTRA_N, ecall, 2500, warm=False),
+                           "read_ceiling": read_ceiling(nv, torch, Ne, Ke)}
+            del re_
+            torch.cuda.empty_cache()
+        result["extra_shapes"] = extra
 
     result["sweep"] = sweeps
     if not args.no_cpu_baseline:

@@ -320,3 +320,23 @@ def test_ffn_down_token_identity(ffn_down):
     full = y_bits(nv.gemv(pw, Xd))
     for n in (1, 3, 8):
         assert np.array_equal(y_bits(nv.gemv(pw, Xd[:n].contiguous())), full[:n]), n
+
+
+# ---- the small hidden-2048 attention layer ----------------------------------------
+
+@pytest.mark.parametrize("n", [1, 16])
+def test_small_attention_shapes(n):
+    """Fused q|k|v 4096|512|512 x 2048 and o_proj 2048 x 4096: fewer row groups
+    than compute units (one per workgroup)."""
+    say("small attention n", n)
+    for N, K, rows in ((5120, 2048, (4096, 512, 512)), (2048, 4096, None)):
+        W, codes, scales, g = weight_case(N, K, 500 + K)
+        pw = packed_from_canonical(codes, scales, g, N, K)
+        X = inputs.activations_bf16(n, K, 600 + n)
+        Yref, Aref = O.gemv(codes, scales, g, X)
+        if rows:
+            off = (0, rows[0], rows[0] + rows[1])
+            Y = y_bits(nv.gemv_qkv(pw, x_to_dev(X), rows, off, N))
+        else:
+            Y = y_bits(nv.gemv(pw, x_to_dev(X)))
+        assert_parity(Y, Yref, Aref, "%dx%d n=%d" % (N, K, n))
