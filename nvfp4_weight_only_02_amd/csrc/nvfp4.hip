@@ -239,16 +239,19 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // Stage X through a per-wave LDS tile into MFMA A-operand layout: lane
     // (i, g) holds X[4*(i%4) + i/4][k .. k+3] with k = 16*block + 4*g, for
     // every block of the slice.  Every X load is older than the MT + 1 ring
-    // loads.  The staging is LDS-bandwidth bound (all waves of a CU stage at
-    // once), so only the NV token quarters in use are written, and only the
-    // lanes whose MFMA row carries one of them read (the other lanes' A rows
-    // stay zero; they only feed outputs that are never stored).
+    // loads; tile t is staged as soon as its own loads are in, while the
+    // later tiles' X and the ring are still arriving.  The staging is
+    // LDS-bandwidth bound (all waves of a CU stage at once), so only the NV
+    // token quarters in use are written, and only the lanes whose MFMA row
+    // carries one of them read (the other lanes' A rows stay zero; they only
+    // feed outputs that are never stored).
     u32x2 xr[MT][kBlocksPerTile];
     const bool xlane = 4 * (i & 3) + (i >> 2) < 4 * NV;
     auto stage_x = [&]() {
     static_for<MT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, MT + 1>{});
+        // Newer than tile t's X loads: the later tiles' X loads and the ring.
+        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, (MT - 1 - t) * NV + MT + 1>{});
 #pragma unroll
         for (int q = 0; q < NV; ++q)
             xstage[wave][q * 4 + (lane >> 4)][chunk] = xg[t][q];
