@@ -141,6 +141,31 @@ int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles);
 int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves,
                           int *tiles_per_wave);
 
+/* Largest token count of one nvfp4_gemm call. */
+#define NVFP4_MAX_GEMM_TOKENS (1 << 20)
+
+/* Prefill / many-token form of the same operation (the step after decode as
+ * n grows: the spark_model::layers page's W4A16 tile GEMMs for prefill, with
+ * tile shapes picked by an occupancy rule):
+ *     Y[t][r] = gscale * sum_k X[t][k] * e2m1(code[r][k]) * e4m3(scale[r][k/16])
+ * for any 1 <= n <= NVFP4_MAX_GEMM_TOKENS.  Same packed weight (nvfp4_pack),
+ * X bf16 [n][K] and Y bf16 [n][N] (row-major, contiguous) as nvfp4_gemv.
+ * The weight is dequantised exactly to bf16 once per token tile (32, 64 or
+ * 128 tokens) and multiplied with MFMA, fp32 accumulation over all of K.
+ * Each token's result is bit-identical whatever n and its place in the batch
+ * (the sum over K runs in one fixed order), but it is a different rounding
+ * order from nvfp4_gemv's (both within the documented fp32 error bound).
+ * Errors: NULL, RANGE (n, N, K), SHAPE (K % 16, K > 262144), ALIGN (Wq,
+ * Wscale, X 16-byte; Y 2-byte), DEVICE, LAUNCH. */
+int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+               const uint16_t *X, uint16_t *Y, int n, int N, int K, void *stream);
+
+/* Tile shape and grid nvfp4_gemm uses for (n, N, K) on MI355X: weight rows
+ * and tokens per workgroup, workgroups along rows and along tokens.  Pure host
+ * function; returns a status. */
+int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup,
+                        int *tokens_per_workgroup, int *grid_x, int *grid_y);
+
 /* Measurement aid, not part of the GEMV path: reads `bytes` bytes of `buf`
  * (DEVICE, 16-byte aligned, bytes a positive multiple of 16) once with the
  * streaming pattern that reads fastest on MI355X (1024-thread workgroups,

@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_launch_geometry.restype = _i32
         L.nvfp4_launch_geometry.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32),
                                             ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        L.nvfp4_gemm.restype = _i32
+        L.nvfp4_gemm.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _vp]
+        L.nvfp4_gemm_geometry.restype = _i32
+        L.nvfp4_gemm_geometry.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.nvfp4_read_stream.restype = _i32
         L.nvfp4_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.nvfp4_strerror.restype = ctypes.c_char_p
@@ -140,6 +145,14 @@ def launch_geometry(n: int, N: int, K: int):
     _check(lib().nvfp4_launch_geometry(n, N, K, ctypes.byref(wg), ctypes.byref(wv),
                                        ctypes.byref(tpw)), "nvfp4_launch_geometry")
     return wg.value, wv.value, tpw.value
+
+
+def gemm_geometry(n: int, N: int, K: int):
+    """(rows per workgroup, tokens per workgroup, grid_x, grid_y) of nvfp4_gemm."""
+    r, t, gx, gy = _i32(), _i32(), _i32(), _i32()
+    _check(lib().nvfp4_gemm_geometry(n, N, K, ctypes.byref(r), ctypes.byref(t), ctypes.byref(gx),
+                                     ctypes.byref(gy)), "nvfp4_gemm_geometry")
+    return r.value, t.value, gx.value, gy.value
 
 
 # ---- weight preparation ----------------------------------------------------
@@ -228,6 +241,20 @@ def gemv_sched(w: PackedWeight, X: torch.Tensor, tile_widths, out: torch.Tensor 
     _check(lib().nvfp4_gemv_sched(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                                   Y.data_ptr(), n, w.N, w.K, widths, len(tile_widths),
                                   _stream(stream)), "nvfp4_gemv_sched")
+    return Y
+
+
+def gemm(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Prefill form: Y[n, N] = X[n, K] . dequant(W)^T for any n >= 1 (tiled
+    MFMA GEMM; bf16 in and out, fp32 accumulation)."""
+    _x(X, w.K)
+    n = X.shape[0]
+    Y = out if out is not None else torch.empty((n, w.N), dtype=torch.bfloat16, device=X.device)
+    _dev(Y, torch.bfloat16, "out")
+    if Y.shape != (n, w.N):
+        raise ValueError("out must be [n, N]")
+    _check(lib().nvfp4_gemm(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
+                            Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemm")
     return Y
 
 

@@ -38,9 +38,9 @@ def hipcc() -> str:
 
 
 def check_resources(remarks: str) -> None:
-    """Refuse a build in which a GEMV kernel spills registers or uses scratch.
+    """Refuse a build in which a GEMV or GEMM kernel spills registers or uses scratch.
 
-    The GEMV kernels issue their vector-memory loads as inline assembly and
+    These kernels issue their vector-memory loads as inline assembly and
     wait for them with explicit vmcnt counts; the compiler does not know such
     a load is still in flight, so a spill (or any other copy) of its
     destination registers before the wait would read them too early."""
@@ -51,13 +51,13 @@ def check_resources(remarks: str) -> None:
         if m:
             kernel = m.group(1)
             continue
-        if kernel is None or "gemv_kernel" not in kernel:
+        if kernel is None or ("gemv_kernel" not in kernel and "gemm_kernel" not in kernel):
             continue
         m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
         if m and int(m.group(2)) != 0:
             bad.append("%s: %s = %s" % (kernel, m.group(1), m.group(2)))
     if bad:
-        raise RuntimeError("GEMV kernels must not spill or use scratch:\n  " + "\n  ".join(bad))
+        raise RuntimeError("GEMV/GEMM kernels must not spill or use scratch:\n  " + "\n  ".join(bad))
 
 
 def build(verbose: bool = False) -> str:

@@ -57,6 +57,7 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerGroup = 16;      // MFMA N dimension: weight rows per tile
 constexpr int kTileK = 128;            // K columns per tile (8 NVFP4 blocks)
@@ -423,6 +424,216 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     }
 }
 
+// ---- prefill: token-tiled GEMM for n beyond one decode tile ----------------
+//
+// The step after the decode path as n grows (the pages' W4A16 tile GEMM
+// family for prefill, sized by a measured occupancy rule): Y = X . dequant(W)^T
+// for any number of tokens.  Here each wave dequantises its weight tile once
+// per token tile, exactly, into bf16 (an E2M1 code times an E4M3 scale has at
+// most 6 significant bits), so the block scale costs nothing per token and one
+// v_mfma_f32_16x16x32_bf16 covers two 16-element blocks, with the fp32 sum
+// carried in the accumulator across all of K.  The packed device layout is
+// the decode path's: dword j of a lane's 16 code bytes holds its 4 + 4 codes
+// of blocks 2j and 2j+1, which is exactly the B operand of one such MFMA when
+// the lane's A operand holds X at the same K positions (a fixed permutation of
+// K inside each pair of blocks, applied to X as it is staged into LDS).
+struct GemmParams {
+    const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
+    const u32x2 *scales;   // packed scales, [RG][T][16 rows] x 8 B
+    const uint16_t *X;     // bf16 [n][K]
+    uint16_t *Y;           // bf16 [n][N]
+    float gscale;
+    int n, N, K, T, RG;
+};
+
+constexpr int kGemmWaves = 4;                 // waves per workgroup, one per SIMD
+constexpr int kXRow = kTileK * 2 + 16;        // LDS bytes of one token's 128-column X slice (+16 pad)
+
+// A wave-uniform value the compiler cannot prove uniform, moved to SGPRs.
+__device__ __forceinline__ u32x4 uniform(u32x4 v)
+{
+    return u32x4{(u32)__builtin_amdgcn_readfirstlane((int)v[0]), (u32)__builtin_amdgcn_readfirstlane((int)v[1]),
+                 (u32)__builtin_amdgcn_readfirstlane((int)v[2]), (u32)__builtin_amdgcn_readfirstlane((int)v[3])};
+}
+
+__device__ __forceinline__ u32x2 buffer_load_b64_nt(u32x4 rsrc, unsigned off)
+{
+    u32x2 v;
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen nt" : "=v"(v) : "v"(off), "s"(rsrc));
+    return v;
+}
+
+// Exact bf16 of the 8 weights of one lane for blocks 2j and 2j+1: codes in
+// dword `w` (bytes 0, 1: block 2j; bytes 2, 3: block 2j+1; low nibble first),
+// E4M3 scales of the two blocks in bytes 2H, 2H+1 of `sw`.
+template <bool H>
+__device__ __forceinline__ u32x4 dequant_pair(u32 w, u32 sw)
+{
+    const auto s2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, H);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const bf16x2 o0 = {(__bf16)(a[0] * s2[0]), (__bf16)(a[1] * s2[0])};
+    const bf16x2 o1 = {(__bf16)(b[0] * s2[0]), (__bf16)(b[1] * s2[0])};
+    const bf16x2 o2 = {(__bf16)(c[0] * s2[1]), (__bf16)(c[1] * s2[1])};
+    const bf16x2 o3 = {(__bf16)(d[0] * s2[1]), (__bf16)(d[1] * s2[1])};
+    return u32x4{__builtin_bit_cast(u32, o0), __builtin_bit_cast(u32, o1), __builtin_bit_cast(u32, o2),
+                 __builtin_bit_cast(u32, o3)};
+}
+
+// Steps of K whose loads are in flight ahead of the one computing: X and
+// weights share one distance (loads complete in issue order).  Smaller token
+// tiles compute less per step, so they prefetch deeper.
+template <int BMB>
+constexpr int gemm_prefetch()
+{
+    return BMB == 2 ? 8 : (BMB == 4 ? 6 : 3);
+}
+
+// One workgroup: 4 waves x RGW row groups (64*RGW weight rows) times a tile of
+// BM = 16*BMB tokens.  Per 128-column K step the workgroup stages the token
+// tile's X slice in LDS (double-buffered), each wave converts its RGW code
+// tiles to bf16 operands and runs 4 * RGW * BMB MFMAs.  The loads of step
+// s + P are issued when step s has computed, into the register slot step s
+// used (a ring of P steps; steps past the end of K load zeros without memory
+// traffic, so every step issues the same loads and every wait count is a
+// constant).  Each output's sum runs over K in the same order whatever n, the
+// tile shape or the token's place in its tile.
+template <int RGW, int BMB>
+__global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams p)
+{
+    constexpr int BM = BMB * 16;
+    constexpr int P = gemm_prefetch<BMB>();
+    constexpr int L = BMB + 2 * RGW;   // loads per step and thread
+    static_assert((P - 1) * L <= 63, "vmcnt is a 6-bit field");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: buffer resources in SGPRs
+    const int i = lane & 15, g = lane >> 4;
+    const int rgw0 = (blockIdx.x * kGemmWaves + wave) * RGW;   // first row group of this wave
+    const int tok0 = blockIdx.y * BM;
+    const int ntok = min(BM, p.n - tok0);
+    const int nrg = max(0, min(RGW, p.RG - rgw0));
+    const int rgb = min(rgw0, p.RG);
+    // Loads past these ranges (row groups beyond RG, tokens beyond n, K
+    // columns beyond K) read zeros without touching memory.
+    const u32x4 crsrc = uniform(buffer_rsrc(p.codes + (size_t)rgb * p.T * 64, (unsigned)(nrg * p.T) * 1024u));
+    const u32x4 srsrc = uniform(buffer_rsrc(reinterpret_cast<const char *>(p.scales) + (size_t)rgb * p.T * 128,
+                                            (unsigned)(nrg * p.T) * 128u));
+    const u32x4 xrsrc = uniform(buffer_rsrc(p.X + (size_t)tok0 * p.K, (unsigned)(ntok * p.K * 2)));
+
+    // X staging: thread tid moves 16-byte chunk c = tid % 16 (columns
+    // 8c .. 8c+7 of the step) of token rows tid/16 + 16u.  Columns 4g' .. 4g'+3
+    // of block b go to the 16-byte A fragment of lane group g' for block pair
+    // b/2, at byte 8*(b%2) of it.
+    __shared__ __align__(16) char xs[2][BM * kXRow];
+    const int c = tid & 15;
+    const int xrow0 = tid >> 4;
+    const int wofs = 64 * (c >> 2) + 32 * (c & 1) + 8 * ((c >> 1) & 1);
+    u32x4 xg[P][BMB];
+    u32x4 cw[P][RGW];
+    u32x2 sw[P][RGW];
+
+    auto issue = [&](auto slot_c, int s) {
+        constexpr int q = decltype(slot_c)::value;
+        const bool live = s < p.T;
+#pragma unroll
+        for (int u = 0; u < BMB; ++u) {
+            const int row = xrow0 + 16 * u;
+            const int k = s * kTileK + 8 * c;
+            xg[q][u] = buffer_load_b128(xrsrc, live && row < ntok && k < p.K ? (unsigned)(row * p.K + k) * 2u
+                                                                           : kOutOfRange);
+        }
+#pragma unroll
+        for (int r = 0; r < RGW; ++r) {
+            cw[q][r] = buffer_load_b128_nt(crsrc, live ? (unsigned)(((r * p.T + s) * 64 + lane) * 16) : kOutOfRange);
+            sw[q][r] = buffer_load_b64_nt(srsrc, live ? (unsigned)(((r * p.T + s) * 16 + i) * 8) : kOutOfRange);
+        }
+    };
+    // Wait until the loads of slot q are in (the P - 1 newer steps' loads may
+    // still be in flight), then move its X into LDS buffer `buf`.
+    auto land = [&](auto slot_c, int buf) {
+        constexpr int q = decltype(slot_c)::value;
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * L) : "memory");
+#pragma unroll
+        for (int u = 0; u < BMB; ++u)
+            asm volatile("" : "+v"(xg[q][u]));
+#pragma unroll
+        for (int r = 0; r < RGW; ++r)
+            asm volatile("" : "+v"(cw[q][r]), "+v"(sw[q][r]));
+#pragma unroll
+        for (int u = 0; u < BMB; ++u) {
+            char *dst = xs[buf] + (xrow0 + 16 * u) * kXRow + wofs;
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{xg[q][u][0], xg[q][u][1]};
+            *reinterpret_cast<u32x2 *>(dst + 16) = u32x2{xg[q][u][2], xg[q][u][3]};
+        }
+    };
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RGW][BMB];
+#pragma unroll
+    for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int tb = 0; tb < BMB; ++tb)
+            acc[r][tb] = zero;
+
+    // One K step from LDS buffer `buf` and weight slot q.
+    auto compute = [&](auto slot_c, int buf) {
+        constexpr int q = decltype(slot_c)::value;
+        const char *xb = xs[buf] + i * kXRow + 16 * g;
+        static_for<4>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            bf16x8 bop[RGW];
+#pragma unroll
+            for (int r = 0; r < RGW; ++r)
+                bop[r] = __builtin_bit_cast(bf16x8, dequant_pair<(j & 1) != 0>(cw[q][r][j], sw[q][r][j >> 1]));
+#pragma unroll
+            for (int tb = 0; tb < BMB; ++tb) {
+                const bf16x8 aop = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow + 64 * j);
+#pragma unroll
+                for (int r = 0; r < RGW; ++r)
+                    acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[r], acc[r][tb], 0, 0, 0);
+            }
+        });
+    };
+
+    static_for<P>([&](auto qc) { issue(qc, decltype(qc)::value); });
+    land(std::integral_constant<int, 0>{}, 0);
+    __syncthreads();
+    for (int s0 = 0; s0 < p.T; s0 += P) {
+        static_for<P>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int s = s0 + q;
+            if (s < p.T) {
+                compute(qc, s & 1);
+                issue(qc, s + P);
+                land(std::integral_constant<int, (q + 1) % P>{}, (s + 1) & 1);
+                __syncthreads();
+            }
+        });
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's trailing loads read nothing
+
+    // Component v of lane (g, i) of acc[r][tb]: token tok0 + 16*tb + 4*g + v,
+    // weight row 16*(rgw0 + r) + i.
+#pragma unroll
+    for (int r = 0; r < RGW; ++r) {
+        const int row = (rgw0 + r) * kRowsPerGroup + i;
+        if (row >= p.N)
+            continue;
+#pragma unroll
+        for (int tb = 0; tb < BMB; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = 16 * tb + 4 * g + v;
+                if (t < ntok)
+                    p.Y[(size_t)(tok0 + t) * p.N + row] = f32_to_bf16_bits(p.gscale * acc[r][tb][v]);
+            }
+    }
+}
+
 // ---- pack: canonical -> tiled device layout --------------------------------
 
 // One thread per 16-byte lane chunk of a tile.
@@ -743,6 +954,58 @@ int launch_gemv(const GemvParams &p, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
+typedef void (*GemmKernel)(GemmParams);
+
+struct GemmGeometry {
+    int rgw, bmb;          // row groups per wave, 16-token blocks per token tile
+    int grid_x, grid_y;    // row tiles, token tiles
+};
+
+// Tile shape of the prefill GEMM for n tokens of an N x K weight on `cus`
+// compute units.  The token tile is the smallest of 32 / 64 / 128 tokens that
+// holds n (capped at 128); the row tile is 128 rows (two row groups per wave)
+// when that still gives every compute unit a workgroup, else 64 rows (the
+// narrow tile for grids that would under-fill the chip).
+void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
+{
+    geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
+    const int bm = 16 * geo->bmb;
+    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    geo->grid_y = (n + bm - 1) / bm;
+    const long long wide = (RG + 2 * kGemmWaves - 1) / (2 * kGemmWaves);
+    geo->rgw = wide * geo->grid_y >= cus ? 2 : 1;
+    geo->grid_x = (int)((RG + geo->rgw * kGemmWaves - 1) / (geo->rgw * kGemmWaves));
+}
+
+template <int RGW>
+GemmKernel pick_gemm_bmb(int bmb)
+{
+    switch (bmb) {
+    case 2: return nvfp4_gemm_kernel<RGW, 2>;
+    case 4: return nvfp4_gemm_kernel<RGW, 4>;
+    default: return nvfp4_gemm_kernel<RGW, 8>;
+    }
+}
+
+GemmKernel pick_gemm(const GemmGeometry &geo)
+{
+    return geo.rgw == 2 ? pick_gemm_bmb<2>(geo.bmb) : pick_gemm_bmb<1>(geo.bmb);
+}
+
+int validate_gemm(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X, const uint16_t *Y,
+                  int n, int N, int K)
+{
+    if (!Wq || !Wscale || !X || !Y)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_GEMM_TOKENS || N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0 || K > kMaxK)
+        return NVFP4_ERR_SHAPE;
+    if (!aligned(Wq, 16) || !aligned(Wscale, 16) || !aligned(X, 16) || !aligned(Y, 2))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
 GemvParams make_params(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
                        uint16_t *Y, int n, int N, int K)
 {
@@ -916,6 +1179,52 @@ int nvfp4_gemv_sched(const uint8_t *Wq, const uint8_t *Wscale, float gscale, con
             return st;
         t0 += tile_widths[j];
     }
+    return NVFP4_OK;
+}
+
+int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X, uint16_t *Y,
+               int n, int N, int K, void *stream)
+{
+    int st = validate_gemm(Wq, Wscale, X, Y, n, N, K);
+    if (st != NVFP4_OK)
+        return st;
+    int cus = 0;
+    st = current_device_info(&cus);
+    if (st != NVFP4_OK)
+        return st;
+    GemmGeometry geo;
+    gemm_geometry_for(n, N, cus, &geo);
+    GemmParams p;
+    p.codes = reinterpret_cast<const u32x4 *>(Wq);
+    p.scales = reinterpret_cast<const u32x2 *>(Wscale);
+    p.X = X;
+    p.Y = Y;
+    p.gscale = gscale;
+    p.n = n;
+    p.N = N;
+    p.K = K;
+    p.T = (K + kTileK - 1) / kTileK;
+    p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    hipLaunchKernelGGL(pick_gemm(geo), dim3(geo.grid_x, geo.grid_y), dim3(kGemmWaves * 64), 0,
+                       (hipStream_t)stream, p);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup, int *tokens_per_workgroup,
+                        int *grid_x, int *grid_y)
+{
+    if (!rows_per_workgroup || !tokens_per_workgroup || !grid_x || !grid_y)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_MAX_GEMM_TOKENS || N < 1 || K < 1)
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0 || K > kMaxK)
+        return NVFP4_ERR_SHAPE;
+    GemmGeometry geo;
+    gemm_geometry_for(n, N, 256, &geo);   // MI355X; the launch itself uses the queried count
+    *rows_per_workgroup = geo.rgw * kGemmWaves * kRowsPerGroup;
+    *tokens_per_workgroup = geo.bmb * 16;
+    *grid_x = geo.grid_x;
+    *grid_y = geo.grid_y;
     return NVFP4_OK;
 }
 

@@ -87,6 +87,39 @@ def test_gemv_validation(args, status):
     assert nv.lib().nvfp4_gemv(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, FAKE, 1.0, FAKE, FAKE, 17, 16, 16), 1),                    # null Wq
+    ((FAKE, FAKE, 1.0, FAKE, 0, 17, 16, 16), 1),                    # null Y
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 0, 16, 16), 2),                  # n = 0
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, (1 << 20) + 1, 16, 16), 2),      # n beyond NVFP4_MAX_GEMM_TOKENS
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 17, -1, 16), 2),                 # N < 1
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 17, 16, 40), 4),                 # K % 16
+    ((FAKE, FAKE, 1.0, FAKE, FAKE, 17, 16, (1 << 18) + 16), 4),     # K too long
+    ((FAKE, FAKE + 4, 1.0, FAKE, FAKE, 17, 16, 16), 3),             # Wscale misaligned
+    ((FAKE, FAKE, 1.0, FAKE + 8, FAKE, 17, 16, 16), 3),             # X not 16-byte aligned
+    ((FAKE, FAKE, 1.0, FAKE, FAKE + 1, 17, 16, 16), 3),             # Y misaligned
+])
+def test_gemm_validation(args, status):
+    assert nv.lib().nvfp4_gemm(*args, None) == status
+
+
+def test_gemm_geometry_rule():
+    # token tile: smallest of 32 / 64 / 128 holding n (capped at 128)
+    assert nv.gemm_geometry(17, 14336, 5120)[1] == 32
+    assert nv.gemm_geometry(64, 14336, 5120)[1] == 64
+    assert nv.gemm_geometry(65, 14336, 5120)[1] == 128
+    assert nv.gemm_geometry(1000, 14336, 5120)[1] == 128
+    # 896 row groups: 128-row tiles give 112 x 1 workgroups at n = 128, which
+    # would leave the chip under-filled, so the narrow 64-row tile is used
+    assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)
+    # with 4 token tiles the wide tile already fills 256 compute units
+    assert nv.gemm_geometry(512, 14336, 5120) == (128, 128, 112, 4)
+    r, t, gx, gy = nv.gemm_geometry(300, 37, 144)    # ragged: 3 row groups, 3 token tiles
+    assert gx * r >= 37 and gy * t >= 300
+    with pytest.raises(nv.Nvfp4Error):
+        nv.gemm_geometry(0, 16, 16)
+
+
 def test_qkv_validation():
     L = nv.lib()
     rows = (ctypes.c_int32 * 3)(32, 16, 16)
