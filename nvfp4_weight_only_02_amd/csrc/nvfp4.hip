@@ -447,7 +447,8 @@ struct GemmParams {
 };
 
 constexpr int kGemmWaves = 4;                 // waves per workgroup, one per SIMD
-constexpr int kXRow = kTileK * 2 + 16;        // LDS bytes of one token's 128-column X slice (+16 pad)
+constexpr int kXRow = kTileK * 2 + 32;        // LDS bytes of one token's 128-column X slice, padded
+                                              // (measured: half the bank conflicts of +16)
 
 // A wave-uniform value the compiler cannot prove uniform, moved to SGPRs.
 __device__ __forceinline__ u32x4 uniform(u32x4 v)
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
             acc[r][tb] = zero;
 
     // One K step from LDS buffer `buf` and weight slot q.
-    auto compute = [&](auto slot_c, int buf) {
+    auto compute_plain = [&](auto slot_c, int buf) {
         constexpr int q = decltype(slot_c)::value;
         const char *xb = xs[buf] + i * kXRow + 16 * g;
         static_for<4>([&](auto jc) {
@@ -597,6 +598,49 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
                     acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[r], acc[r][tb], 0, 0, 0);
             }
         });
+    };
+
+    // One K step from LDS buffer `buf` and weight slot q, software-pipelined
+    // over its four 32-column substeps: the A fragments and the dequantised B
+    // operands of substep j+1 are produced while substep j's MFMAs run.
+    auto compute_pipe = [&](auto slot_c, int buf) {
+        constexpr int q = decltype(slot_c)::value;
+        const char *xb = xs[buf] + i * kXRow + 16 * g;
+        bf16x8 a[2][BMB], b[2][RGW];
+#pragma unroll
+        for (int tb = 0; tb < BMB; ++tb)
+            a[0][tb] = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow);
+#pragma unroll
+        for (int r = 0; r < RGW; ++r)
+            b[0][r] = __builtin_bit_cast(bf16x8, dequant_pair<false>(cw[q][r][0], sw[q][r][0]));
+        static_for<4>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int cur = j & 1, nxt = cur ^ 1;
+            if constexpr (j < 3) {
+#pragma unroll
+                for (int tb = 0; tb < BMB; ++tb)
+                    a[nxt][tb] = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow + 64 * (j + 1));
+#pragma unroll
+                for (int r = 0; r < RGW; ++r)
+                    b[nxt][r] = __builtin_bit_cast(bf16x8, dequant_pair<((j + 1) & 1) != 0>(cw[q][r][j + 1], sw[q][r][(j + 1) >> 1]));
+            }
+#pragma unroll
+            for (int tb = 0; tb < BMB; ++tb)
+#pragma unroll
+                for (int r = 0; r < RGW; ++r)
+                    acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][tb], b[cur][r], acc[r][tb], 0, 0, 0);
+            
+        });
+    };
+
+    // The pipelined form needs two more A and B register sets; with two row
+    // groups per wave that would drop the kernel to one wave per SIMD, which
+    // measured slower than the plain form.
+    auto compute = [&](auto slot_c, int buf) {
+        if constexpr (RGW == 1)
+            compute_pipe(slot_c, buf);
+        else
+            compute_plain(slot_c, buf);
     };
 
     static_for<P>([&](auto qc) { issue(qc, decltype(qc)::value); });
