@@ -27,7 +27,9 @@ Also measured (default; --quick skips them):
   * the achievable read ceiling of each shape (nvfp4_read_stream over the
     same bytes, same rotation) and the CPU oracle on a bounded sample;
   * shapes beyond the decode projections (dense FFN gate+up and down with
-    K > 8192, the pages' small hidden-2048 attention layer) at n = 1..16.
+    K > 8192, the pages' small hidden-2048 attention layer) at n = 1..16;
+  * the prefill GEMM (nvfp4_gemm) on the fused QKV weight at n = 32..2048,
+    against the dense bf16 MFMA peak and against ceil(n/16) decode launches.
 """
 from __future__ import annotations
 
@@ -61,6 +63,8 @@ EXTRA_SHAPES = [
     ("attn_small_o_proj_2048x4096", 2048, 4096, None, "hidden 2048: o_proj"),
 ]
 EXTRA_N = [1, 2, 4, 8, 16]
+# Prefill (many-token) GEMM sweep on the fused QKV weight.
+PREFILL_N = [32, 64, 128, 256, 512, 1024, 2048]
 ROTATION_BYTES = 1 << 30
 SETTLE_S = 0.03
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_n16_counters.json")
@@ -234,6 +238,37 @@ def sweep_shape(torch, rot, n_list, call, x_seed, row_scale=False, warm=True):
     return out
 
 
+def prefill_sweep(nv, torch, t_gemv16):
+    """nvfp4_gemm on the fused QKV weight for n beyond one decode tile: cold
+    rotation, time per call, MFMA throughput against the dense bf16 peak, and
+    the time ceil(n/16) decode launches of 16 tokens would take (t_gemv16
+    each), which is what the decode kernel alone would cost."""
+    from nvfp4_weight_only_02_amd import metrics
+    N, K = SHAPES["fused_qkv_14336x5120"]
+    rp = Rotation(nv, torch, N, K, seed=8100)
+    out = {}
+    for n in PREFILL_N:
+        X = make_x(torch, n, K, 2600 + n)
+        Y = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
+        if n == PREFILL_N[0]:
+            gs = capture(torch, lambda i: nv.gemm(rp.copies[i % rp.count], X, out=Y), rp.count)
+            settle(torch, gs)
+            del gs
+        t = time_calls(torch, lambda i: nv.gemm(rp.copies[i % rp.count], X, out=Y), rp.count)
+        tf = metrics.flops(n, N, K) / t / 1e12
+        rows, toks, gx, gy = nv.gemm_geometry(n, N, K)
+        out[str(n)] = {"us": round(t * 1e6, 3), "TFLOPs": round(tf, 1),
+                       "frac_bf16_mfma_peak": round(tf / metrics.BF16_DENSE_TFLOPS, 4),
+                       "tokens_per_s": round(n / t, 1),
+                       "weight_GBps_once": round(metrics.weight_bytes(N, K) / t / 1e9, 1),
+                       "decode_launches_us": round(math.ceil(n / 16) * t_gemv16 * 1e6, 3),
+                       "tile": {"rows": rows, "tokens": toks, "grid": [gx, gy]}}
+        del X, Y
+    del rp
+    torch.cuda.empty_cache()
+    return out
+
+
 def read_ceiling(nv, torch, N, K):
     """Seconds per read of one weight's bytes with nvfp4_read_stream, over a
     >= 1 GiB rotation of distinct buffers (the same cold regime)."""
@@ -340,6 +375,8 @@ def main():
     ap.add_argument("--workload", default="fused_qkv_14336x5120", choices=sorted(SHAPES))
     ap.add_argument("--sweep", default=",".join(str(v) for v in range(1, 17)),
                     help="token counts of the per-n sweeps ('' = none)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="headline timing, then only the prefill GEMM sweep (for profiling it)")
     ap.add_argument("--quick", action="store_true",
                     help="headline and its per-n sweep only (no other shapes, schedules, decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -447,6 +484,11 @@ def main():
     if args.profile_only:
         print(json.dumps(result), flush=True)
         return
+    if args.prefill_only:
+        del rot
+        torch.cuda.empty_cache()
+        print(json.dumps({"prefill_fused_qkv": prefill_sweep(nv, torch, t_call)}), flush=True)
+        return
 
     n_list = [int(v) for v in args.sweep.split(",") if v.strip()]
     sweeps = {}
@@ -523,6 +565,9 @@ def main():
             del re_
             torch.cuda.empty_cache()
         result["extra_shapes"] = extra
+
+        log("prefill GEMM sweep ...")
+        result["prefill_fused_qkv"] = prefill_sweep(nv, torch, t_call)
 
     result["sweep"] = sweeps
     if not args.no_cpu_baseline:
