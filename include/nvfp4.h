@@ -80,6 +80,24 @@ size_t nvfp4_packed_scales_bytes(int N, int K);
 int nvfp4_quantize(const float *W, int N, int K, uint8_t *codes, uint8_t *scales,
                    float *tensor_scale, void *stream);
 
+/* Input element types of nvfp4_quantize_packed. */
+#define NVFP4_DTYPE_F32 0
+#define NVFP4_DTYPE_BF16 1
+
+/* The same recipe as nvfp4_quantize, writing the packed device layout
+ * directly (no canonical copy, no nvfp4_pack pass): the pages' runtime
+ * requantisation, whose fix emits the layout the GEMV reads during the
+ * requant (Atlas PR #266 review and follow-up on the transposed copy).  W is
+ * [N][K] row-major, fp32 (dtype NVFP4_DTYPE_F32, finite) or bf16 bit patterns
+ * (NVFP4_DTYPE_BF16, widened to fp32 exactly, so the result is the fp32
+ * recipe on the widened values), 16-byte aligned.  codes_packed /
+ * scales_packed: device buffers of nvfp4_packed_*_bytes(N, K), 16-byte
+ * aligned, byte-identical to nvfp4_pack(nvfp4_quantize(W)) including the zero
+ * padding.  tensor_scale: device float[2] = {gscale, amax}.  Errors: NULL,
+ * RANGE (N, K, dtype), SHAPE (K % 16), ALIGN, DEVICE, LAUNCH. */
+int nvfp4_quantize_packed(const void *W, int dtype, int N, int K, uint8_t *codes_packed,
+                          uint8_t *scales_packed, float *tensor_scale, void *stream);
+
 /* Reorder canonical codes/scales (device) into the packed device layout
  * (device buffers of nvfp4_packed_*_bytes; the padding is written as zeros).
  * One-time, at weight load.  Errors: NULL, RANGE, SHAPE, ALIGN (packed

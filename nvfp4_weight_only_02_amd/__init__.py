@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_packed_scales_bytes.argtypes = [_i32, _i32]
         L.nvfp4_quantize.restype = _i32
         L.nvfp4_quantize.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.nvfp4_quantize_packed.restype = _i32
+        L.nvfp4_quantize_packed.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
         L.nvfp4_pack.restype = _i32
         L.nvfp4_pack.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp]
         L.nvfp4_gemv.restype = _i32
@@ -172,6 +174,24 @@ def quantize(W: torch.Tensor, stream=None):
     return codes, scales, ts
 
 
+def quantize_packed(W: torch.Tensor, stream=None):
+    """fp32 or bf16 [N, K] (device) -> packed device layout directly
+    (codes, scales, tensor_scale f32[2] = [gscale, amax]), all on the device."""
+    if not isinstance(W, torch.Tensor) or W.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("W must be a float32 or bfloat16 tensor")
+    _dev(W, W.dtype, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    cp = torch.empty(packed_codes_bytes(N, K), dtype=torch.uint8, device=W.device)
+    sp = torch.empty(packed_scales_bytes(N, K), dtype=torch.uint8, device=W.device)
+    ts = torch.empty(2, dtype=torch.float32, device=W.device)
+    dtype = 0 if W.dtype == torch.float32 else 1
+    _check(lib().nvfp4_quantize_packed(W.data_ptr(), dtype, N, K, cp.data_ptr(), sp.data_ptr(),
+                                       ts.data_ptr(), _stream(stream)), "nvfp4_quantize_packed")
+    return cp, sp, ts
+
+
 def pack(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):
     """Canonical codes/scales (device) -> packed device layout."""
     _dev(codes, torch.uint8, "codes")
@@ -202,8 +222,8 @@ class PackedWeight:
 
     @classmethod
     def from_float(cls, W: torch.Tensor, stream=None) -> "PackedWeight":
-        codes, scales, ts = quantize(W, stream)
-        cp, sp = pack(codes, scales, W.shape[0], W.shape[1], stream)
+        """Quantise an fp32 or bf16 weight straight into the packed layout."""
+        cp, sp, ts = quantize_packed(W, stream)
         gscale = float(ts[0].item())          # one host read at load time
         return cls(cp, sp, gscale, W.shape[0], W.shape[1])
 

@@ -830,6 +830,94 @@ __global__ void nvfp4_quantize_kernel(const float4 *W, long long nblocks, uint2 
     scales[blk] = (uint8_t)s;
 }
 
+// Fused recipe quantiser writing the packed device layout directly (the
+// pages' runtime requantisation with its "emit the transposed copy during
+// requant" fix, on this layout): one thread per (row group, tile, row) makes
+// the tile's 8 block scales and 128 codes of that row with exactly the
+// decisions of nvfp4_quantize_kernel and stores them where nvfp4_pack would:
+// lane chunk g of the tile holds the row's columns 4g .. 4g+3 of every block
+// (byte 2b + e/2 of the chunk, low nibble first), and the row's 8 scale bytes
+// follow in block order.  Rows past N and blocks past K/16 are zero.
+template <typename T>
+__device__ __forceinline__ float load_w(const T *W, long long idx);
+template <>
+__device__ __forceinline__ float load_w<float>(const float *W, long long idx)
+{
+    return W[idx];
+}
+template <>
+__device__ __forceinline__ float load_w<uint16_t>(const uint16_t *W, long long idx)
+{
+    return __uint_as_float((u32)W[idx] << 16);   // bf16 -> fp32, exact
+}
+
+template <typename T>
+__global__ void nvfp4_quantize_packed_kernel(const T *W, int N, int K, int T_tiles, long long items,
+                                             const float *ts, u32x4 *codes, u32x2 *scales)
+{
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= items)
+        return;
+    const int i = (int)(idx & 15);
+    const long long tile_lin = idx >> 4;
+    const int tile = (int)(tile_lin % T_tiles);
+    const long long rg = tile_lin / T_tiles;
+    const long long row = rg * kRowsPerGroup + i;
+    const int nb = K / 16;
+    const float gs = (float)((double)ts[1] / 2688.0);
+    u32 chunk[4][4] = {};
+    u32 sb[2] = {0u, 0u};
+#pragma unroll 1
+    for (int b = 0; b < kBlocksPerTile; ++b) {
+        const int blk = tile * kBlocksPerTile + b;
+        if (row >= N || blk >= nb)
+            continue;
+        float w[16];
+        const long long base = row * (long long)K + (long long)blk * 16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            w[e] = load_w<T>(W, base + e);
+        double am = 0.0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            am = fmax(am, fabs((double)w[e]));
+        const int sc = gs > 0.0f ? e4m3_rne(am / (6.0 * (double)gs)) : 0;
+        const double d = e4m3_value(sc) * (double)gs;
+        sb[b >> 2] |= (u32)sc << (8 * (b & 3));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int mag = d > 0.0 ? e2m1_rne(fabs((double)w[e]), d) : 0;
+            const u32 code = (u32)mag | (signbit(w[e]) ? 8u : 0u);
+            const int g = e >> 2;
+            const int byte = 2 * (b & 1) + ((e & 3) >> 1);
+            chunk[g][b >> 1] |= code << (8 * byte + 4 * (e & 1));
+        }
+    }
+    const long long tbase = (rg * T_tiles + tile) * 64;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        codes[tbase + g * 16 + i] = u32x4{chunk[g][0], chunk[g][1], chunk[g][2], chunk[g][3]};
+    scales[(rg * T_tiles + tile) * 16 + i] = u32x2{sb[0], sb[1]};
+}
+
+template <typename T>
+__global__ void nvfp4_amax_any_kernel(const T *W, long long n, float *ts)
+{
+    float m = 0.0f;
+    for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < n;
+         j += (long long)gridDim.x * blockDim.x)
+        m = fmaxf(m, fabsf(load_w<T>(W, j)));
+    for (int o = 32; o > 0; o >>= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0)   // non-negative floats order like their bit patterns
+        atomicMax(reinterpret_cast<unsigned int *>(ts + 1), __float_as_uint(m));
+}
+
+__global__ void nvfp4_gscale_kernel(float *ts)
+{
+    ts[0] = (float)((double)ts[1] / 2688.0);
+}
+
 // ---- read-stream ceiling (measurement aid) ------------------------------------
 
 constexpr int kReadThreads = 1024;
@@ -1133,6 +1221,50 @@ int nvfp4_quantize(const float *W, int N, int K, uint8_t *codes, uint8_t *scales
     hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const float4 *>(W), nblocks, reinterpret_cast<uint2 *>(codes),
                        scales, tensor_scale);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_quantize_packed(const void *W, int dtype, int N, int K, uint8_t *codes_packed,
+                          uint8_t *scales_packed, float *tensor_scale, void *stream)
+{
+    if (!W || !codes_packed || !scales_packed || !tensor_scale)
+        return NVFP4_ERR_NULL;
+    if (N < 1 || K < 1 || (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16))
+        return NVFP4_ERR_RANGE;
+    if (K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(codes_packed, 16) || !aligned(scales_packed, 16) ||
+        !aligned(tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    int cus = 0;
+    int st = current_device_info(&cus);
+    if (st != NVFP4_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const long long n = (long long)N * K;
+    long long grid = (n + 255) / 256;
+    if (grid > (long long)cus * 8)
+        grid = (long long)cus * 8;
+    const int T = (K + kTileK - 1) / kTileK;
+    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const long long items = RG * T * 16;
+    const unsigned qgrid = (unsigned)((items + 255) / 256);
+    hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+    if (dtype == NVFP4_DTYPE_F32) {
+        const float *w = reinterpret_cast<const float *>(W);
+        hipLaunchKernelGGL(nvfp4_amax_any_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, w, n, tensor_scale);
+        hipLaunchKernelGGL(nvfp4_quantize_packed_kernel<float>, dim3(qgrid), dim3(256), 0, s, w, N, K, T, items,
+                           tensor_scale, reinterpret_cast<u32x4 *>(codes_packed),
+                           reinterpret_cast<u32x2 *>(scales_packed));
+    } else {
+        const uint16_t *w = reinterpret_cast<const uint16_t *>(W);
+        hipLaunchKernelGGL(nvfp4_amax_any_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, w, n,
+                           tensor_scale);
+        hipLaunchKernelGGL(nvfp4_quantize_packed_kernel<uint16_t>, dim3(qgrid), dim3(256), 0, s, w, N, K, T,
+                           items, tensor_scale, reinterpret_cast<u32x4 *>(codes_packed),
+                           reinterpret_cast<u32x2 *>(scales_packed));
+    }
+    hipLaunchKernelGGL(nvfp4_gscale_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

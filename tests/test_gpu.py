@@ -103,6 +103,37 @@ def test_quantize_matches_oracle(N, K, kind):
     assert float(ts[1].item()) == float(np.abs(W).max())
 
 
+@pytest.mark.parametrize("N,K,kind", [
+    (1024, 1024, "f32"), (37, 144, "f32"), (1, 16, "f32"), (300, 6160, "f32_zero_outlier"),
+    (64, 64, "zeros"), (45, 656, "bf16"), (1024, 1024, "bf16")])
+def test_quantize_packed_equals_quantize_then_pack(N, K, kind):
+    """The fused quantiser writes the packed layout byte for byte as
+    pack(quantize(W)) would (padding included), and quantize(W) is the
+    oracle's recipe bit for bit (test above); bf16 input is the recipe on
+    the exactly widened values."""
+    say("quantize_packed", N, K, kind)
+    if kind == "zeros":
+        W = np.zeros((N, K), dtype=np.float32)
+    else:
+        W = inputs.weights_f32(N, K, 11)
+        if kind == "f32_zero_outlier":
+            W = inputs.add_zero_and_outlier_blocks(W, 12)
+    if kind == "bf16":
+        Wd = torch.from_numpy(W).cuda().to(torch.bfloat16)
+        W32 = inputs.bf16_bits_to_f32(Wd.view(torch.int16).cpu().numpy().view(np.uint16))
+    else:
+        Wd = torch.from_numpy(W).cuda()
+        W32 = W
+    cp, sp, ts = nv.quantize_packed(Wd)
+    codes, scales, g = O.quantize(W32)
+    pw = packed_from_canonical(codes, scales, g, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, pw.codes)
+    assert torch.equal(sp, pw.scales)
+    assert float(ts[0].item()) == g
+    assert float(ts[1].item()) == float(np.abs(W32).max())
+
+
 # ---- GEMV parity -----------------------------------------------------------------
 
 @pytest.mark.parametrize("n", list(range(1, 17)))

@@ -120,6 +120,20 @@ def test_gemm_geometry_rule():
         nv.gemm_geometry(0, 16, 16)
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 16, 16, FAKE, FAKE, FAKE), 1),            # null W
+    ((FAKE, 0, 16, 16, FAKE, 0, FAKE), 1),            # null packed scales
+    ((FAKE, 2, 16, 16, FAKE, FAKE, FAKE), 2),         # unknown dtype
+    ((FAKE, 0, 0, 16, FAKE, FAKE, FAKE), 2),          # N = 0
+    ((FAKE, 1, 16, 40, FAKE, FAKE, FAKE), 4),         # K % 16
+    ((FAKE + 8, 0, 16, 16, FAKE, FAKE, FAKE), 3),     # W not 16-byte aligned
+    ((FAKE, 0, 16, 16, FAKE + 4, FAKE, FAKE), 3),     # packed codes misaligned
+    ((FAKE, 1, 16, 16, FAKE, FAKE, FAKE + 2), 3),     # tensor scale misaligned
+])
+def test_quantize_packed_validation(args, status):
+    assert nv.lib().nvfp4_quantize_packed(*args, None) == status
+
+
 def test_qkv_validation():
     L = nv.lib()
     rows = (ctypes.c_int32 * 3)(32, 16, 16)
