@@ -224,12 +224,16 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // contiguous scale bytes of the slice (lane l holds bytes 16l .. 16l+15).
     u32x4 wsc;
     u32x4 wc[MT];
-    auto scale_off = [&](int rgl) -> unsigned {
-        return lane < 8 * tw ? (unsigned)((rgl * p.T + tw0) * 128 + lane * 16) : kOutOfRange;
+    // Offsets of row group rgl of the K-slice that starts at tile w0 and
+    // holds wn tiles.
+    auto scale_off_at = [&](int rgl, int w0, int wn) -> unsigned {
+        return lane < 8 * wn ? (unsigned)((rgl * p.T + w0) * 128 + lane * 16) : kOutOfRange;
     };
-    auto code_off = [&](int rgl, int t) -> unsigned {
-        return (EXACT || t < tw) ? (unsigned)((rgl * p.T + tw0 + t) * 1024 + lane * 16) : kOutOfRange;
+    auto code_off_at = [&](int rgl, int t, int w0, int wn) -> unsigned {
+        return (EXACT || t < wn) ? (unsigned)((rgl * p.T + w0 + t) * 1024 + lane * 16) : kOutOfRange;
     };
+    auto scale_off = [&](int rgl) -> unsigned { return scale_off_at(rgl, tw0, tw); };
+    auto code_off = [&](int rgl, int t) -> unsigned { return code_off_at(rgl, t, tw0, tw); };
     auto issue_ring = [&](int rgl) {
         wsc = buffer_load_b128_nt(srsrc, scale_off(rgl));
 #pragma unroll
@@ -248,11 +252,16 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // feed outputs that are never stored).
     u32x2 xr[MT][kBlocksPerTile];
     const bool xlane = 4 * (i & 3) + (i >> 2) < 4 * NV;
-    auto stage_x = [&]() {
+    // RING_FIRST: this pass's ring was issued before its X loads (by the
+    // previous pass), so only the later tiles' X loads are newer than tile t's.
+    auto stage_x = [&](auto ring_first_tag) {
+    constexpr bool RING_FIRST = decltype(ring_first_tag)::value;
     static_for<MT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        // Newer than tile t's X loads: the later tiles' X loads and the ring.
-        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3], std::integral_constant<int, (MT - 1 - t) * NV + MT + 1>{});
+        // Newer than tile t's X loads: the later tiles' X loads and (unless
+        // it was issued first) the ring.
+        vm_wait4(xg[t][0], xg[t][1], xg[t][2], xg[t][3],
+                 std::integral_constant<int, (MT - 1 - t) * NV + (RING_FIRST ? 0 : MT + 1)>{});
 #pragma unroll
         for (int q = 0; q < NV; ++q)
             xstage[wave][q * 4 + (lane >> 4)][chunk] = xg[t][q];
@@ -282,13 +291,13 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     // last row group nothing is refilled and the counts fall as it drains.
     // Blocks run as a software pipeline (the scale FMA of a block trails its
     // MFMA by two blocks).
-    auto rowgroup = [&](auto refill_tag, int rg) -> f32x4 {
+    auto rowgroup = [&](auto refill_tag, int rg, int nrgl, int nw0, int nwn) -> f32x4 {
         constexpr bool REFILL = decltype(refill_tag)::value;
         vm_wait1(wsc, std::integral_constant<int, MT>{});
         sstage[wave][lane] = wsc;
         asm volatile("" ::: "memory");
         if constexpr (REFILL)
-            wsc = buffer_load_b128_nt(srsrc, scale_off(rg - rg0 + 1));
+            wsc = buffer_load_b128_nt(srsrc, scale_off_at(nrgl, nw0, nwn));
         const char *sbase = reinterpret_cast<const char *>(&sstage[wave][0]) + i * 8;
         f32x4 acc = zero, p1 = zero, p2 = zero;
         float s1 = 0.f, s2 = 0.f;
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
             // Refill the slot once its codes are consumed, so the next
             // row group's tile lands in the same registers.
             if constexpr (REFILL)
-                wc[t] = buffer_load_b128_nt(crsrc, code_off(rg - rg0 + 1, t));
+                wc[t] = buffer_load_b128_nt(crsrc, code_off_at(nrgl, t, nw0, nwn));
         });
 #pragma unroll
         for (int v = 0; v < NV; ++v)
@@ -390,20 +399,52 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
             __syncthreads();
     };
     if constexpr (CHUNKED) {
-        for (int b0 = rg0; b0 < rg1; b0 += kSlots) {
-            const int b1 = min(b0 + kSlots, rg1);
-            for (int c = 0; c < p.kc; ++c) {
-                tw0 = (c * W + wave) * MT;
-                tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
-                issue_x();
-                issue_ring(b0 - rg0);
-                stage_x();
-                for (int rg = b0; rg < b1 - 1; ++rg)
-                    park(rg - b0, c, rowgroup(std::true_type{}, rg));
-                park(b1 - 1 - b0, c, rowgroup(std::false_type{}, b1 - 1));
+        // Work items (batch of up to kSlots row groups, K chunk c, row group)
+        // in order, one row-group call site: every row group refills the ring
+        // with the next item's tiles -- the next row group of this pass, else
+        // the first row group of the next pass (next chunk, else the next
+        // batch's first chunk) -- so only the first pass starts on an empty
+        // ring; after the last item the refill offsets lie past the buffer
+        // resources (loads that read nothing) and are drained at the end.
+        int b0 = rg0, b1 = min(rg0 + kSlots, rg1), c = 0, rg = rg0;
+        tw0 = wave * MT;
+        tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+        issue_x();
+        issue_ring(0);
+        stage_x(std::false_type{});
+        while (true) {
+            int nb0 = b0, nb1 = b1, nc = c, nrg = rg + 1;
+            if (nrg == b1) {
+                nrg = b0;
+                nc = c + 1;
+                if (nc == p.kc) {
+                    nc = 0;
+                    nb0 = b1;
+                    nb1 = min(b1 + kSlots, rg1);
+                    nrg = nb0;
+                }
             }
-            batch_end(b0, b1);
+            const bool more = nb0 < rg1;
+            const int nw0 = (nc * W + wave) * MT;
+            const int nwn = more ? (EXACT ? MT : max(0, min(MT, p.T - nw0))) : 0;
+            park(rg - b0, c, rowgroup(std::true_type{}, rg, more ? nrg - rg0 : rg1 - rg0, nw0, nwn));
+            if (rg == b1 - 1 && c == p.kc - 1)
+                batch_end(b0, b1);
+            if (!more)
+                break;
+            const bool new_pass = nc != c || nb0 != b0;
+            b0 = nb0;
+            b1 = nb1;
+            c = nc;
+            rg = nrg;
+            if (new_pass) {
+                tw0 = nw0;
+                tw = nwn;
+                issue_x();
+                stage_x(std::true_type{});
+            }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
         // One K chunk: X is loaded and staged once for the whole launch, and
         // the ring runs on across batches (each slot refilled with the next
@@ -411,7 +452,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
         issue_x();
         issue_ring(0);
-        stage_x();
+        stage_x(std::false_type{});
         auto finish = [&](int rg, const f32x4 acc) {
             const int slot = (rg - rg0) % kSlots;
             park(slot, 0, acc);
@@ -419,8 +460,8 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 batch_end(rg - slot, rg + 1);
         };
         for (int rg = rg0; rg < rg1 - 1; ++rg)
-            finish(rg, rowgroup(std::true_type{}, rg));
-        finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1));
+            finish(rg, rowgroup(std::true_type{}, rg, rg - rg0 + 1, tw0, tw));
+        finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1, 0, 0, 0));
     }
 }
 
@@ -956,8 +997,9 @@ template <int MT, int NV>
 GemvKernel pick_exact(bool exact, bool chunked)
 {
     // Several chunks imply more than 64 tiles split into chunks of at most
-    // kMaxTilesChunked tiles per wave, so 5 <= MT <= kMaxTilesChunked.
-    if constexpr (MT >= 5 && MT <= kMaxTilesChunked) {
+    // kMaxTilesChunked tiles per wave: 4 <= MT <= kMaxTilesChunked for every
+    // K up to 262144.
+    if constexpr (MT >= 4 && MT <= kMaxTilesChunked) {
         if (chunked)
             return exact ? nvfp4_gemv_kernel<MT, NV, true, true> : nvfp4_gemv_kernel<MT, NV, false, true>;
     }
