@@ -218,9 +218,12 @@ def test_token_result_independent_of_n(qkvz):
     for t in range(16):
         one = y_bits(nv.gemv(pw, Xd[t:t + 1].contiguous()))
         assert np.array_equal(one[0], full[t]), t
-    for n in (2, 3, 4, 8, 15):
+    for n in range(1, 16):
         part = y_bits(nv.gemv(pw, Xd[:n].contiguous()))
         assert np.array_equal(part, full[:n]), n
+    for a in (3, 9):   # a window of tokens that does not start at token 0
+        part = y_bits(nv.gemv(pw, Xd[a:16].contiguous()))
+        assert np.array_equal(part, full[a:16]), a
 
 
 @pytest.mark.parametrize("sched", [[3, 3, 3, 3, 3, 1], [16], [8, 8], [4, 4, 4, 4], [1] * 16, [5, 11]])

@@ -147,3 +147,40 @@ def test_gemm_full_size_sampled(n):
     err = np.abs(Y[ts, rs] - yref)
     tol = O.tolerance(yref, aref)
     assert (err <= tol).all(), float(np.max(err / tol))
+
+
+def test_gemm_permutation_negation_scaling():
+    """Token permutation permutes rows, negating X negates Y, X * 8 and
+    gscale / 4 scale Y exactly (all bit for bit)."""
+    say("gemm invariants 700x2048 n=90")
+    N, K, n = 700, 2048, 90
+    W = inputs.weights_f32(N, K, 61)
+    codes, scales, g = O.quantize(W)
+    pw = packed(codes, scales, g, N, K)
+    X = inputs.activations_bf16(n, K, 62)
+    ref = y_bits(nv.gemm(pw, x_to_dev(X)))
+    perm = np.random.default_rng(4).permutation(n)
+    assert np.array_equal(y_bits(nv.gemm(pw, x_to_dev(X[perm]))), ref[perm])
+    assert np.array_equal(y_bits(nv.gemm(pw, x_to_dev(X ^ np.uint16(0x8000)))), ref ^ np.uint16(0x8000))
+    X8 = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(X) * np.float32(8))
+    assert np.array_equal(O.bf16_bits_to_f64(y_bits(nv.gemm(pw, x_to_dev(X8)))), 8 * O.bf16_bits_to_f64(ref))
+    pw4 = nv.PackedWeight(pw.codes, pw.scales, pw.gscale * 0.25, N, K)
+    assert np.array_equal(O.bf16_bits_to_f64(y_bits(nv.gemm(pw4, x_to_dev(X)))),
+                          0.25 * O.bf16_bits_to_f64(ref))
+
+
+@pytest.mark.parametrize("n", [17, 200])
+def test_gemm_guard_band_untouched(n):
+    """Canaries before and after Y stay intact (ragged last row and token tiles)."""
+    say("gemm guard band 1000x1024 n", n)
+    N, K, G = 1000, 1024, 4096
+    W = inputs.weights_f32(N, K, 71)
+    codes, scales, g = O.quantize(W)
+    pw = packed(codes, scales, g, N, K)
+    X = inputs.activations_bf16(n, K, 72)
+    buf = torch.full((G + n * N + G,), 3.0, dtype=torch.bfloat16, device="cuda")
+    nv.gemm(pw, x_to_dev(X), out=buf[G:G + n * N].view(n, N))
+    b = O.bf16_bits_to_f64(y_bits(buf))
+    assert (b[:G] == 3.0).all() and (b[G + n * N:] == 3.0).all()
+    Yref, Aref = O.gemv(codes, scales, g, X)
+    assert_parity(y_bits(buf[G:G + n * N].view(n, N)), Yref, Aref, "guard band n=%d" % n)
