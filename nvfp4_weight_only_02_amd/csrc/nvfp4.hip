@@ -487,7 +487,7 @@ struct GemmParams {
     int n, N, K, T, RG;
 };
 
-constexpr int kGemmWaves = 4;                 // waves per workgroup, one per SIMD
+
 constexpr int kXRow = kTileK * 2 + 32;        // LDS bytes of one token's 128-column X slice, padded
                                               // (measured: half the bank conflicts of +16)
 
@@ -543,18 +543,19 @@ constexpr int gemm_prefetch()
 // traffic, so every step issues the same loads and every wait count is a
 // constant).  Each output's sum runs over K in the same order whatever n, the
 // tile shape or the token's place in its tile.
-template <int RGW, int BMB>
-__global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams p)
+template <int RGW, int BMB, int GW>
+__global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
 {
     constexpr int BM = BMB * 16;
     constexpr int P = gemm_prefetch<BMB>();
-    constexpr int L = BMB + 2 * RGW;   // loads per step and thread
+    constexpr int L = 4 * BMB / GW + 2 * RGW;   // loads per step and thread
     static_assert((P - 1) * L <= 63, "vmcnt is a 6-bit field");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: buffer resources in SGPRs
     const int i = lane & 15, g = lane >> 4;
-    const int rgw0 = (blockIdx.x * kGemmWaves + wave) * RGW;   // first row group of this wave
+    constexpr int XL = 4 * BMB / GW;   // X chunks per thread and step
+    const int rgw0 = (blockIdx.x * GW + wave) * RGW;   // first row group of this wave
     const int tok0 = blockIdx.y * BM;
     const int ntok = min(BM, p.n - tok0);
     const int nrg = max(0, min(RGW, p.RG - rgw0));
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
     const int c = tid & 15;
     const int xrow0 = tid >> 4;
     const int wofs = 64 * (c >> 2) + 32 * (c & 1) + 8 * ((c >> 1) & 1);
-    u32x4 xg[P][BMB];
+    u32x4 xg[P][XL];
     u32x4 cw[P][RGW];
     u32x2 sw[P][RGW];
 
@@ -582,8 +583,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
         constexpr int q = decltype(slot_c)::value;
         const bool live = s < p.T;
 #pragma unroll
-        for (int u = 0; u < BMB; ++u) {
-            const int row = xrow0 + 16 * u;
+        for (int u = 0; u < XL; ++u) {
+            const int row = xrow0 + 4 * GW * u;
             const int k = s * kTileK + 8 * c;
             xg[q][u] = buffer_load_b128(xrsrc, live && row < ntok && k < p.K ? (unsigned)(row * p.K + k) * 2u
                                                                            : kOutOfRange);
@@ -600,14 +601,14 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
         constexpr int q = decltype(slot_c)::value;
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * L) : "memory");
 #pragma unroll
-        for (int u = 0; u < BMB; ++u)
+        for (int u = 0; u < XL; ++u)
             asm volatile("" : "+v"(xg[q][u]));
 #pragma unroll
         for (int r = 0; r < RGW; ++r)
             asm volatile("" : "+v"(cw[q][r]), "+v"(sw[q][r]));
 #pragma unroll
-        for (int u = 0; u < BMB; ++u) {
-            char *dst = xs[buf] + (xrow0 + 16 * u) * kXRow + wofs;
+        for (int u = 0; u < XL; ++u) {
+            char *dst = xs[buf] + (xrow0 + 4 * GW * u) * kXRow + wofs;
             *reinterpret_cast<u32x2 *>(dst) = u32x2{xg[q][u][0], xg[q][u][1]};
             *reinterpret_cast<u32x2 *>(dst + 16) = u32x2{xg[q][u][2], xg[q][u][3]};
         }
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void nvfp4_gemm_kernel(GemmParams 
     // groups per wave that would drop the kernel to one wave per SIMD, which
     // measured slower than the plain form.
     auto compute = [&](auto slot_c, int buf) {
-        if constexpr (RGW == 1)
+        if constexpr (RGW == 1 || GW == 8)
             compute_pipe(slot_c, buf);
         else
             compute_plain(slot_c, buf);
@@ -1131,39 +1132,51 @@ int launch_gemv(const GemvParams &p, hipStream_t stream)
 typedef void (*GemmKernel)(GemmParams);
 
 struct GemmGeometry {
-    int rgw, bmb;          // row groups per wave, 16-token blocks per token tile
+    int rgw, gw, bmb;      // row groups per wave, waves per workgroup, 16-token blocks per token tile
     int grid_x, grid_y;    // row tiles, token tiles
 };
 
 // Tile shape of the prefill GEMM for n tokens of an N x K weight on `cus`
 // compute units.  The token tile is the smallest of 32 / 64 / 128 tokens that
-// holds n (capped at 128); the row tile is 128 rows (two row groups per wave)
-// when that still gives every compute unit a workgroup, else 64 rows (the
-// narrow tile for grids that would under-fill the chip).
+// holds n (capped at 128).  The row tile is the largest of 256 rows (8 waves x
+// 2 row groups), 128 rows (4 x 2) and 64 rows (4 x 1) that still gives every
+// compute unit a workgroup (narrower tiles for grids that would under-fill
+// the chip; larger tiles read X fewer times per flop).
 void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
 {
     geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
     const int bm = 16 * geo->bmb;
     const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
     geo->grid_y = (n + bm - 1) / bm;
-    const long long wide = (RG + 2 * kGemmWaves - 1) / (2 * kGemmWaves);
-    geo->rgw = wide * geo->grid_y >= cus ? 2 : 1;
-    geo->grid_x = (int)((RG + geo->rgw * kGemmWaves - 1) / (geo->rgw * kGemmWaves));
+    static const int shapes[3][2] = {{2, 8}, {2, 4}, {1, 4}};   // (row groups per wave, waves)
+    int pick = 2;
+    for (int j = 0; j < 3; ++j) {
+        const long long tiles = (RG + shapes[j][0] * shapes[j][1] - 1) / (shapes[j][0] * shapes[j][1]);
+        if (tiles * geo->grid_y >= cus) {
+            pick = j;
+            break;
+        }
+    }
+    geo->rgw = shapes[pick][0];
+    geo->gw = shapes[pick][1];
+    geo->grid_x = (int)((RG + geo->rgw * geo->gw - 1) / (geo->rgw * geo->gw));
 }
 
-template <int RGW>
+template <int RGW, int GW>
 GemmKernel pick_gemm_bmb(int bmb)
 {
     switch (bmb) {
-    case 2: return nvfp4_gemm_kernel<RGW, 2>;
-    case 4: return nvfp4_gemm_kernel<RGW, 4>;
-    default: return nvfp4_gemm_kernel<RGW, 8>;
+    case 2: return nvfp4_gemm_kernel<RGW, 2, GW>;
+    case 4: return nvfp4_gemm_kernel<RGW, 4, GW>;
+    default: return nvfp4_gemm_kernel<RGW, 8, GW>;
     }
 }
 
 GemmKernel pick_gemm(const GemmGeometry &geo)
 {
-    return geo.rgw == 2 ? pick_gemm_bmb<2>(geo.bmb) : pick_gemm_bmb<1>(geo.bmb);
+    if (geo.rgw == 2)
+        return geo.gw == 8 ? pick_gemm_bmb<2, 8>(geo.bmb) : pick_gemm_bmb<2, 4>(geo.bmb);
+    return pick_gemm_bmb<1, 4>(geo.bmb);
 }
 
 int validate_gemm(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X, const uint16_t *Y,
@@ -1423,7 +1436,8 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uin
     p.K = K;
     p.T = (K + kTileK - 1) / kTileK;
     p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    hipLaunchKernelGGL(pick_gemm(geo), dim3(geo.grid_x, geo.grid_y), dim3(kGemmWaves * 64), 0,
+    hipLaunchKernelGGL(pick_gemm(geo), dim3(geo.grid_x, geo.grid_y),
+                       dim3(geo.gw * 64), 0,
                        (hipStream_t)stream, p);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
@@ -1439,7 +1453,7 @@ int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup, int *token
         return NVFP4_ERR_SHAPE;
     GemmGeometry geo;
     gemm_geometry_for(n, N, 256, &geo);   // MI355X; the launch itself uses the queried count
-    *rows_per_workgroup = geo.rgw * kGemmWaves * kRowsPerGroup;
+    *rows_per_workgroup = geo.rgw * geo.gw * kRowsPerGroup;
     *tokens_per_workgroup = geo.bmb * 16;
     *grid_x = geo.grid_x;
     *grid_y = geo.grid_y;

@@ -184,3 +184,19 @@ def test_gemm_guard_band_untouched(n):
     assert (b[:G] == 3.0).all() and (b[G + n * N:] == 3.0).all()
     Yref, Aref = O.gemv(codes, scales, g, X)
     assert_parity(y_bits(buf[G:G + n * N].view(n, N)), Yref, Aref, "guard band n=%d" % n)
+
+
+def test_gemm_identity_across_row_tiles_full_size():
+    """Fused QKV weight: n = 40 (64-row tile), 300 (128-row tile) and 1024
+    (256-row tile, 8 waves) give the same bits for the tokens they share."""
+    N, K = 14336, 5120
+    shapes = [nv.gemm_geometry(n, N, K)[0] for n in (40, 300, 1024)]
+    say("gemm row tiles", shapes)
+    assert shapes == [64, 128, 256]
+    W = inputs.weights_f32(N, K, inputs.weight_seed(1))
+    codes, scales, g = O.quantize(W)
+    pw = packed(codes, scales, g, N, K)
+    X = x_to_dev(inputs.activations_bf16(1024, K, 81))
+    big = y_bits(nv.gemm(pw, X))
+    for n in (40, 300):
+        assert np.array_equal(y_bits(nv.gemm(pw, X[:n].contiguous())), big[:n]), n

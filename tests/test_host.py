@@ -112,8 +112,11 @@ def test_gemm_geometry_rule():
     # 896 row groups: 128-row tiles give 112 x 1 workgroups at n = 128, which
     # would leave the chip under-filled, so the narrow 64-row tile is used
     assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)
-    # with 4 token tiles the wide tile already fills 256 compute units
+    # with 4 token tiles the 256-row tile would give 224 workgroups, the
+    # 128-row tile 448: the largest tile that fills the chip wins
     assert nv.gemm_geometry(512, 14336, 5120) == (128, 128, 112, 4)
+    # with 8 token tiles the 256-row tile (8 waves) already fills it
+    assert nv.gemm_geometry(1024, 14336, 5120) == (256, 128, 56, 8)
     r, t, gx, gy = nv.gemm_geometry(300, 37, 144)    # ragged: 3 row groups, 3 token tiles
     assert gx * r >= 37 and gy * t >= 300
     with pytest.raises(nv.Nvfp4Error):
