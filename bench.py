@@ -76,8 +76,11 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+_T0 = time.perf_counter()
+
+
 def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+    print("[%6.1f s]" % (time.perf_counter() - _T0), *a, file=sys.stderr, flush=True)
 
 
 def zero_outlier_(torch, W, gen, frac=0.01, factor=50.0):
