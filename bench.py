@@ -27,7 +27,8 @@ Also measured (default; --quick skips them):
   * the achievable read ceiling of each shape (nvfp4_read_stream over the
     same bytes, same rotation) and the CPU oracle on a bounded sample;
   * shapes beyond the decode projections (dense FFN gate+up and down with
-    K > 8192, the pages' small hidden-2048 attention layer) at n = 1..16;
+    K > 8192, the latter also in K parts through nvfp4_gemv_ws, the pages'
+    small hidden-2048 attention layer) at n = 1..16;
   * the prefill GEMM (nvfp4_gemm) on the fused QKV weight at n = 32..2048,
     against the dense bf16 MFMA peak and against ceil(n/16) decode launches.
 """
@@ -58,7 +59,8 @@ QKV_OFFS = (0, 8192, 11264)
 # query heads and 2 KV heads of dimension 256.
 EXTRA_SHAPES = [
     ("ffn_gate_up_34816x5120", 34816, 5120, None, "dense FFN gate+up fused, intermediate 17408"),
-    ("ffn_down_5120x17408", 5120, 17408, None, "dense FFN down, K in 3 chunk passes"),
+    ("ffn_down_5120x17408", 5120, 17408, None,
+     "dense FFN down: K in 3 chunk passes (nvfp4_gemv), or in K parts (nvfp4_gemv_ws)"),
     ("attn_small_qkv_5120x2048", 5120, 2048, (4096, 512, 512), "hidden 2048: fused q|k|v 4096|512|512"),
     ("attn_small_o_proj_2048x4096", 2048, 4096, None, "hidden 2048: o_proj"),
 ]
@@ -565,6 +567,16 @@ def main():
                            "launch": {"workgroups": wg_, "tiles_per_wave": tpw_},
                            "sweep": sweep_shape(torch, re_, EXTRA_N, ecall, 2500, warm=False),
                            "read_ceiling": read_ceiling(nv, torch, Ne, Ke)}
+            ks = nv.gemv_kparts(Ne, Ke)
+            if ks > 1 and not rows:
+                # K parts: partials in a workspace allocated once, outside the
+                # captured graphs, then the fixed-order reduction launch.
+                ws = torch.empty(nv.gemv_workspace_bytes(max(EXTRA_N), Ne, Ke, ks), dtype=torch.uint8,
+                                 device="cuda")
+                kcall = (lambda k_, ws_: lambda w, X, Y: nv.gemv_ws(w, X, k_, ws_, out=Y))(ks, ws)
+                extra[name]["k_parts"] = {"ks": ks, "entry": "nvfp4_gemv_ws",
+                                          "sweep": sweep_shape(torch, re_, EXTRA_N, kcall, 2500, warm=False)}
+                del ws
             del re_
             torch.cuda.empty_cache()
         result["extra_shapes"] = extra

@@ -57,7 +57,8 @@ typedef enum {
     NVFP4_ERR_SHAPE = 4,     /* K not a multiple of 16, or a size limit         */
     NVFP4_ERR_SCHEDULE = 5,  /* an explicit tile schedule is invalid            */
     NVFP4_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch               */
-    NVFP4_ERR_DEVICE = 7     /* the current device is not a gfx950 GPU          */
+    NVFP4_ERR_DEVICE = 7,    /* the current device is not a gfx950 GPU          */
+    NVFP4_ERR_WORKSPACE = 8  /* a required workspace is NULL or too small       */
 } nvfp4_status;
 
 /* Largest number of tokens one launch covers (the decode batch of the pages:
@@ -115,6 +116,42 @@ int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K,
  * a workgroup's share of the weight beyond 2 GiB), ALIGN, LAUNCH, DEVICE. */
 int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
                const uint16_t *X, uint16_t *Y, int n, int N, int K, void *stream);
+
+/* nvfp4_gemv with the K dimension cut into ks parts, for long-K projections
+ * such as a dense FFN's down projection (the dense-FFN decode paths of the
+ * spark_model::layers page's FfnComponent dispatch).  One launch computes the
+ * fp32 partial of each (K part, 16-row group) unit into `workspace`
+ * ([ks][n][N] fp32, DEVICE, 16-byte aligned, at least
+ * nvfp4_gemv_workspace_bytes(n, N, K, ks) bytes, owned by the caller); a
+ * second launch on the same stream adds the parts in part
+ * order, scales by gscale and rounds to bf16.  The parts fill the chip where
+ * N alone has fewer 16-row groups than there are compute units and cut the
+ * share of X each compute unit loads.  ks = 0 takes nvfp4_gemv_kparts(N, K);
+ * ks = 1 is exactly nvfp4_gemv (no workspace needed, none touched).  The sum
+ * order depends only on (N, K, ks), so each token's result is bit-identical
+ * to the same token alone (n = 1) at the same ks; across different ks the
+ * rounding order differs (all within the documented fp32 error bound).
+ * Calls that share a workspace on different streams race.  Errors: as
+ * nvfp4_gemv; RANGE (ks < 0 or ks > 64), SHAPE (with T = ceil(K/128) and
+ * tp = ceil(T/ks) tiles per part: a part would be empty, ks > T or
+ * (ks-1)*tp >= T, or longer than one pass, ks > 1 and tp > 64),
+ * WORKSPACE (ks > 1 and workspace NULL or too small), ALIGN (workspace). */
+int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+                  const uint16_t *X, uint16_t *Y, int n, int N, int K, int ks,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* K parts nvfp4_gemv_ws takes for ks = 0, from the shape alone: 1 while K <=
+ * 8192 (one pass of the 8 waves' X slices); beyond, the part count that
+ * minimises (rounds of 16-row groups per compute unit of MI355X's 256) x
+ * (128-column tiles per part) with every part within one pass, the fewest on
+ * a tie (4 for 5120 x 17408).  Pure host function; returns ks >= 1 or a
+ * negative status (-RANGE, -SHAPE). */
+int nvfp4_gemv_kparts(int N, int K);
+
+/* Bytes of workspace nvfp4_gemv_ws needs for (n, N, K, ks): ks * n * N * 4
+ * for ks > 1 (ks = 0: nvfp4_gemv_kparts), 0 for ks = 1 and for invalid
+ * arguments.  Pure host function. */
+size_t nvfp4_gemv_workspace_bytes(int n, int N, int K, int ks);
 
 /* Fused QKV projection (Atlas PR #266, PR description, multi_seq/qkv.rs
  * bullet: one fused weight whose q, k and v rows land at fixed offsets of a

@@ -25,7 +25,7 @@ MAX_TOKENS = 16
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_RANGE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_SHAPE", 5: "NVFP4_ERR_SCHEDULE", 6: "NVFP4_ERR_LAUNCH",
-          7: "NVFP4_ERR_DEVICE"}
+          7: "NVFP4_ERR_DEVICE", 8: "NVFP4_ERR_WORKSPACE"}
 
 
 class Nvfp4Error(RuntimeError):
@@ -59,6 +59,13 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_pack.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp]
         L.nvfp4_gemv.restype = _i32
         L.nvfp4_gemv.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _vp]
+        L.nvfp4_gemv_ws.restype = _i32
+        L.nvfp4_gemv_ws.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _vp, ctypes.c_size_t, _vp]
+        L.nvfp4_gemv_kparts.restype = _i32
+        L.nvfp4_gemv_kparts.argtypes = [_i32, _i32]
+        L.nvfp4_gemv_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_gemv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
         L.nvfp4_gemv_qkv.restype = _i32
         L.nvfp4_gemv_qkv.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32,
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
@@ -247,6 +254,40 @@ def gemv(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None
         raise ValueError("out must be [n, N]")
     _check(lib().nvfp4_gemv(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                             Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemv")
+    return Y
+
+
+def gemv_kparts(N: int, K: int) -> int:
+    """K parts gemv_ws takes by default for an N x K weight."""
+    ks = lib().nvfp4_gemv_kparts(N, K)
+    if ks < 0:
+        raise Nvfp4Error(-ks, "nvfp4_gemv_kparts")
+    return ks
+
+
+def gemv_workspace_bytes(n: int, N: int, K: int, ks: int = 0) -> int:
+    """Workspace bytes gemv_ws needs (0 when it needs none)."""
+    return int(lib().nvfp4_gemv_workspace_bytes(n, N, K, ks))
+
+
+def gemv_ws(w: PackedWeight, X: torch.Tensor, ks: int = 0, workspace: torch.Tensor = None,
+            out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """gemv with K cut into ``ks`` parts (0: the library's choice for the
+    shape): fp32 partials in ``workspace`` (a uint8 device tensor, allocated
+    here when not given), then a fixed-order sum of the parts."""
+    _x(X, w.K)
+    n = X.shape[0]
+    Y = out if out is not None else torch.empty((n, w.N), dtype=torch.bfloat16, device=X.device)
+    _dev(Y, torch.bfloat16, "out")
+    if Y.shape != (n, w.N):
+        raise ValueError("out must be [n, N]")
+    if workspace is None:
+        need = gemv_workspace_bytes(n, w.N, w.K, ks)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device)
+    _dev(workspace, torch.uint8, "workspace")
+    _check(lib().nvfp4_gemv_ws(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
+                               Y.data_ptr(), n, w.N, w.K, int(ks), workspace.data_ptr(),
+                               workspace.numel(), _stream(stream)), "nvfp4_gemv_ws")
     return Y
 
 

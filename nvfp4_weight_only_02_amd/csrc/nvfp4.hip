@@ -69,6 +69,7 @@ constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer resource: 32-bit d
 constexpr unsigned kOutOfRange = 0x7FFFFFF0u;   // buffer offset past any resource: reads zeros
 constexpr int kSlots = 8;                        // row-group partials parked in LDS
 constexpr int kMaxK = 1 << 18;                   // keeps every buffer offset within 32 bits
+constexpr int kMaxKParts = 64;                   // K parts of a split launch
 
 struct GemvParams {
     const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
@@ -77,10 +78,15 @@ struct GemvParams {
     uint16_t *Y;           // bf16 output, token stride ldy
     float gscale;
     int n, N, K, T, RG;
-    int kc;                // K chunks (passes): chunk c covers tiles [c*8*MT, (c+1)*8*MT)
+    int kc;                // K chunks (passes) of a K part: chunk c covers its tiles [c*8*MT, (c+1)*8*MT)
     int rg_base, rg_rem;   // row groups per workgroup: rg_base, +1 for the first rg_rem
     int start1, start2;    // first row of the 2nd and 3rd projection (N if absent)
     long long off0, off1, off2, ldy;
+    // K split: workgroups [q*wpp, (q+1)*wpp) own the tiles [q*tp, min((q+1)*tp, T))
+    // of K part q.  With P set they store fp32 partials P[q][t][r] (unscaled)
+    // instead of Y; nvfp4_ksplit_reduce_kernel then sums the parts.
+    int tp, wpp;
+    float *P;
 };
 
 // Two E2M1 codes (byte `sel` of w) -> two bf16 values, unscaled (scale 1.0).
@@ -158,26 +164,34 @@ __device__ __forceinline__ void vm_wait1(u32x4 &a, std::integral_constant<int, N
 // One launch covers every token (n <= 16) of one weight matrix.
 //   MT    tiles of the K-slice each of the kWaves waves owns in one K chunk;
 //   NV    ceil(n / 4): accumulator components that carry real tokens;
-//   EXACT every wave owns exactly MT tiles of every chunk (K == 128 * T,
-//         T == kc * kWaves * MT), so no column predication is needed;
+//   EXACT every wave owns exactly MT tiles of every chunk (of every K part)
+//         (K == 128 * T, T == ks * tp, tp == kc * kWaves * MT), so no column
+//         predication is needed;
 //   CHUNKED K is longer than one chunk (8 waves x 8 tiles, whose X slices
 //         fill the VGPRs): the launch runs kc passes over the workgroup's row
 //         groups, one per K chunk, restaging X for each, and each wave adds
-//         its chunk partials into its own LDS slots in chunk order.
-template <int MT, int NV, bool EXACT, bool CHUNKED>
+//         its chunk partials into its own LDS slots in chunk order;
+//   SPLIT K is cut into parts of at most one chunk each: the workgroups of
+//         part q cover its tiles only and store unscaled fp32 partials, which
+//         nvfp4_ksplit_reduce_kernel sums in part order.
+template <int MT, int NV, bool EXACT, bool CHUNKED, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
 {
+    static_assert(!(SPLIT && CHUNKED), "a K part is one pass");
     constexpr int W = kWaves;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int i = lane & 15;   // MFMA row of A (token 4*(i%4) + i/4), weight row of B and C
     const int g = lane >> 4;   // K quarter of A and B, accumulator token offset of C
 
-    const int wg = blockIdx.x;
+    const int kpart = SPLIT ? (int)blockIdx.x / p.wpp : 0;   // K part: tiles [pt0, pt1)
+    const int wg = SPLIT ? (int)blockIdx.x - kpart * p.wpp : (int)blockIdx.x;
+    const int pt0 = SPLIT ? kpart * p.tp : 0;
+    const int pt1 = SPLIT ? min(p.T, pt0 + p.tp) : p.T;
     const int rg0 = wg * p.rg_base + min(wg, p.rg_rem);
     const int rg1 = rg0 + p.rg_base + (wg < p.rg_rem ? 1 : 0);
-    int tw0 = wave * MT;   // first tile of this wave's slice in the current K chunk
-    int tw = MT;           // tiles of it that exist
+    int tw0 = pt0 + wave * MT;   // first tile of this wave's slice in the current K chunk
+    int tw = MT;                 // tiles of it that exist
 
     // All vector-memory loads of the main path are inline buffer loads waited
     // for with explicit, compile-time vmcnt values: loads retire in issue
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 if (q < NV) {
                     const int row = q * 4 + (lane >> 4);
                     const int k = (tw0 + t) * kTileK + chunk * 8;
-                    const bool ok = row < p.n && (EXACT || k < p.K);
+                    const bool ok = row < p.n && (EXACT || ((!SPLIT || t < tw) && k < p.K));
                     xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
                 }
             }
@@ -360,7 +374,17 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 sum[v] = sum[v] + q[v];
         }
         const int r = rg * kRowsPerGroup + i;
-        if (r < p.N) {
+        if constexpr (SPLIT) {
+            if (r < p.N) {
+                float *dst = p.P + (long long)kpart * p.n * p.N + r;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int tok = 4 * v + g;
+                    if (tok < p.n)
+                        dst[(long long)tok * p.N] = sum[v];
+                }
+            }
+        } else if (r < p.N) {
             long long off;
             if (r >= p.start2)
                 off = p.off2 + (r - p.start2);
@@ -407,8 +431,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         // ring; after the last item the refill offsets lie past the buffer
         // resources (loads that read nothing) and are drained at the end.
         int b0 = rg0, b1 = min(rg0 + kSlots, rg1), c = 0, rg = rg0;
-        tw0 = wave * MT;
-        tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+        tw = EXACT ? MT : max(0, min(MT, pt1 - tw0));
         issue_x();
         issue_ring(0);
         stage_x(std::false_type{});
@@ -425,8 +448,8 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 }
             }
             const bool more = nb0 < rg1;
-            const int nw0 = (nc * W + wave) * MT;
-            const int nwn = more ? (EXACT ? MT : max(0, min(MT, p.T - nw0))) : 0;
+            const int nw0 = pt0 + (nc * W + wave) * MT;
+            const int nwn = more ? (EXACT ? MT : max(0, min(MT, pt1 - nw0))) : 0;
             park(rg - b0, c, rowgroup(std::true_type{}, rg, more ? nrg - rg0 : rg1 - rg0, nw0, nwn));
             if (rg == b1 - 1 && c == p.kc - 1)
                 batch_end(b0, b1);
@@ -449,7 +472,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         // One K chunk: X is loaded and staged once for the whole launch, and
         // the ring runs on across batches (each slot refilled with the next
         // row group whatever batch it belongs to).
-        tw = EXACT ? MT : max(0, min(MT, p.T - tw0));
+        tw = EXACT ? MT : max(0, min(MT, pt1 - tw0));
         issue_x();
         issue_ring(0);
         stage_x(std::false_type{});
@@ -463,6 +486,31 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
             finish(rg, rowgroup(std::true_type{}, rg, rg - rg0 + 1, tw0, tw));
         finish(rg1 - 1, rowgroup(std::false_type{}, rg1 - 1, 0, 0, 0));
     }
+}
+
+// K-split epilogue: Y[t][r] = bf16_RNE(gscale * (((P[0] + P[1]) + P[2]) + ...)),
+// the K parts added in part order, so a token's result depends only on
+// (N, K, ks), never on n.  One thread per output, written at its projection's
+// offset as in the single-launch epilogue.
+__global__ __launch_bounds__(256) void nvfp4_ksplit_reduce_kernel(GemvParams p, int ks)
+{
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;   // t * N + r
+    const long long count = (long long)p.n * p.N;
+    if (e >= count)
+        return;
+    const int t = (int)(e / p.N);
+    const int r = (int)(e - (long long)t * p.N);
+    float s = p.P[e];
+    for (int q = 1; q < ks; ++q)
+        s = s + p.P[q * count + e];
+    long long off;
+    if (r >= p.start2)
+        off = p.off2 + (r - p.start2);
+    else if (r >= p.start1)
+        off = p.off1 + (r - p.start1);
+    else
+        off = p.off0 + r;
+    p.Y[(long long)t * p.ldy + off] = f32_to_bf16_bits(p.gscale * s);
 }
 
 // ---- prefill: token-tiled GEMM for n beyond one decode tile ----------------
@@ -995,48 +1043,53 @@ __global__ __launch_bounds__(kReadThreads) void nvfp4_read_stream_kernel(const u
 typedef void (*GemvKernel)(GemvParams);
 
 template <int MT, int NV>
-GemvKernel pick_exact(bool exact, bool chunked)
+GemvKernel pick_exact(bool exact, bool chunked, bool split)
 {
     // Several chunks imply more than 64 tiles split into chunks of at most
     // kMaxTilesChunked tiles per wave: 4 <= MT <= kMaxTilesChunked for every
-    // K up to 262144.
+    // K up to 262144.  A K part is never chunked.
     if constexpr (MT >= 4 && MT <= kMaxTilesChunked) {
-        if (chunked)
-            return exact ? nvfp4_gemv_kernel<MT, NV, true, true> : nvfp4_gemv_kernel<MT, NV, false, true>;
+        if (chunked && !split)
+            return exact ? nvfp4_gemv_kernel<MT, NV, true, true, false>
+                         : nvfp4_gemv_kernel<MT, NV, false, true, false>;
     }
     if (chunked)
         return nullptr;
-    return exact ? nvfp4_gemv_kernel<MT, NV, true, false> : nvfp4_gemv_kernel<MT, NV, false, false>;
+    if (split)
+        return exact ? nvfp4_gemv_kernel<MT, NV, true, false, true> : nvfp4_gemv_kernel<MT, NV, false, false, true>;
+    return exact ? nvfp4_gemv_kernel<MT, NV, true, false, false> : nvfp4_gemv_kernel<MT, NV, false, false, false>;
 }
 
 template <int NV>
-GemvKernel pick_mt(int mt, bool exact, bool chunked)
+GemvKernel pick_mt(int mt, bool exact, bool chunked, bool split)
 {
     switch (mt) {
-    case 1: return pick_exact<1, NV>(exact, chunked);
-    case 2: return pick_exact<2, NV>(exact, chunked);
-    case 3: return pick_exact<3, NV>(exact, chunked);
-    case 4: return pick_exact<4, NV>(exact, chunked);
-    case 5: return pick_exact<5, NV>(exact, chunked);
-    case 6: return pick_exact<6, NV>(exact, chunked);
-    case 7: return pick_exact<7, NV>(exact, chunked);
-    default: return pick_exact<8, NV>(exact, chunked);
+    case 1: return pick_exact<1, NV>(exact, chunked, split);
+    case 2: return pick_exact<2, NV>(exact, chunked, split);
+    case 3: return pick_exact<3, NV>(exact, chunked, split);
+    case 4: return pick_exact<4, NV>(exact, chunked, split);
+    case 5: return pick_exact<5, NV>(exact, chunked, split);
+    case 6: return pick_exact<6, NV>(exact, chunked, split);
+    case 7: return pick_exact<7, NV>(exact, chunked, split);
+    default: return pick_exact<8, NV>(exact, chunked, split);
     }
 }
 
-// Kernel for n tokens (ceil(n/4) accumulator components) and MT tiles per wave.
-GemvKernel pick_kernel(int n, int mt, bool exact, bool chunked)
+// Kernel for n tokens (ceil(n/4) accumulator components), MT tiles per wave,
+// several K chunks (one launch) or K parts (partials for the reduction).
+GemvKernel pick_kernel(int n, int mt, bool exact, bool chunked, bool split)
 {
     switch ((n + 3) / 4) {
-    case 1: return pick_mt<1>(mt, exact, chunked);
-    case 2: return pick_mt<2>(mt, exact, chunked);
-    case 3: return pick_mt<3>(mt, exact, chunked);
-    default: return pick_mt<4>(mt, exact, chunked);
+    case 1: return pick_mt<1>(mt, exact, chunked, split);
+    case 2: return pick_mt<2>(mt, exact, chunked, split);
+    case 3: return pick_mt<3>(mt, exact, chunked, split);
+    default: return pick_mt<4>(mt, exact, chunked, split);
     }
 }
 
 struct Geometry {
     int workgroups, mt, kc;
+    int ks, tp, wpp;   // K parts, tiles per part, workgroups per part
     bool exact;
 };
 
@@ -1070,20 +1123,64 @@ int current_device_info(int *cus)
 // short), one workgroup per compute unit per round, and as few workgroups as
 // keep the number of rounds (row groups per workgroup) at its minimum, so that
 // every workgroup streams the same number of row groups where N allows it.
-bool geometry_for(int N, int K, int cus, Geometry *geo)
+//
+// With ks > 1 K parts, K's tiles are cut into ks parts of tp tiles (the last
+// possibly shorter, none empty); each (part, row group) is one unit of work
+// and every part gets the same number of workgroups (wpp), each a contiguous
+// row-group range of its part.
+bool geometry_for(int N, int K, int cus, int ks, Geometry *geo)
 {
     const int T = (K + kTileK - 1) / kTileK;
     const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    if (ks < 1 || ks > T)
+        return false;
+    geo->ks = ks;
+    geo->tp = (T + ks - 1) / ks;
+    if ((long long)(ks - 1) * geo->tp >= T)
+        return false;   // the last part would be empty
+    if (ks > 1 && geo->tp > kWaves * kMaxTilesPerWave)
+        return false;   // a K part is one pass
     // One chunk up to 8 tiles per wave; beyond, chunks of at most
     // kMaxTilesChunked tiles per wave (the chunked kernels keep one more
     // set of X registers live across passes).
-    const int per_chunk = T <= kWaves * kMaxTilesPerWave ? kWaves * kMaxTilesPerWave : kWaves * kMaxTilesChunked;
-    geo->kc = (T + per_chunk - 1) / per_chunk;
-    geo->mt = (T + kWaves * geo->kc - 1) / (kWaves * geo->kc);
-    geo->exact = K % kTileK == 0 && T == geo->kc * kWaves * geo->mt;
-    const long long rounds = (RG + cus - 1) / cus;
-    geo->workgroups = (int)((RG + rounds - 1) / rounds);
+    const int tp = geo->tp;
+    const int per_chunk = tp <= kWaves * kMaxTilesPerWave ? kWaves * kMaxTilesPerWave : kWaves * kMaxTilesChunked;
+    geo->kc = (tp + per_chunk - 1) / per_chunk;
+    geo->mt = (tp + kWaves * geo->kc - 1) / (kWaves * geo->kc);
+    geo->exact = K % kTileK == 0 && T == ks * tp && tp == geo->kc * kWaves * geo->mt;
+    const long long rounds = (ks * RG + cus - 1) / cus;
+    geo->wpp = (int)((RG + rounds - 1) / rounds);
+    geo->workgroups = ks * geo->wpp;
     return true;
+}
+
+// K parts for an N x K weight, from the shape alone (so a token's result
+// never depends on n or on the device): one part while a part's tiles fit in
+// one pass (K <= 8192); beyond, the count that minimises the critical path
+// (rounds of row groups per workgroup on MI355X's 256 compute units times the
+// tiles per part) with one pass per part, the fewest parts on a tie.  A
+// single launch restages X once per pass and leaves compute units idle when
+// N has fewer row groups than the chip has units; parts fill the chip and
+// halve (or better) the X each compute unit loads.
+int ksplit_for(int N, int K)
+{
+    const int T = (K + kTileK - 1) / kTileK;
+    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    if (T <= kWaves * kMaxTilesPerWave)
+        return 1;
+    int best = 1;
+    long long best_cost = -1;
+    for (int ks = 2; ks <= T && ks <= kMaxKParts; ++ks) {
+        const int tp = (T + ks - 1) / ks;
+        if ((long long)(ks - 1) * tp >= T || tp > kWaves * kMaxTilesPerWave)
+            continue;
+        const long long cost = ((ks * RG + 255) / 256) * tp;
+        if (best_cost < 0 || cost < best_cost) {
+            best = ks;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 bool aligned(const void *p, size_t a)
@@ -1107,26 +1204,46 @@ int validate_common(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X,
     return NVFP4_OK;
 }
 
-int launch_gemv(const GemvParams &p, hipStream_t stream)
+// Workspace of a launch with ks K parts: fp32 partials [ks][n][N].
+size_t ksplit_workspace_bytes(int ks, int n, int N)
+{
+    return ks > 1 ? (size_t)ks * n * N * sizeof(float) : 0;
+}
+
+// One GEMV launch (ks == 1), or the K-part launch and its reduction (ks > 1,
+// partials in `ws`, which the caller has checked to be large enough).
+int launch_gemv(const GemvParams &p, hipStream_t stream, int ks = 1, void *ws = nullptr)
 {
     int cus = 0;
     int st = current_device_info(&cus);
     if (st != NVFP4_OK)
         return st;
     Geometry geo;
-    if (!geometry_for(p.N, p.K, cus, &geo))
+    if (!geometry_for(p.N, p.K, cus, ks, &geo))
         return NVFP4_ERR_SHAPE;
-    GemvKernel k = pick_kernel(p.n, geo.mt, geo.exact, geo.kc > 1);
+    GemvKernel k = pick_kernel(p.n, geo.mt, geo.exact, geo.kc > 1, ks > 1);
     if (!k)
         return NVFP4_ERR_SHAPE;
     GemvParams q = p;
-    q.rg_base = p.RG / geo.workgroups;
-    q.rg_rem = p.RG % geo.workgroups;
+    q.rg_base = p.RG / geo.wpp;
+    q.rg_rem = p.RG % geo.wpp;
     q.kc = geo.kc;
+    q.tp = geo.tp;
+    q.wpp = geo.wpp;
+    q.P = ks > 1 ? static_cast<float *>(ws) : nullptr;
     if ((long long)(q.rg_base + 1) * p.T * 1024 > 0x7FFFFFFFLL)
         return NVFP4_ERR_SHAPE;   // a workgroup's codes must stay within a 32-bit buffer offset
     hipLaunchKernelGGL(k, dim3(geo.workgroups), dim3(kWaves * 64), 0, stream, q);
-    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess)
+        return NVFP4_ERR_LAUNCH;
+    if (ks > 1) {
+        const long long count = (long long)p.n * p.N;
+        hipLaunchKernelGGL(nvfp4_ksplit_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                           stream, q, ks);
+        if (hipGetLastError() != hipSuccess)
+            return NVFP4_ERR_LAUNCH;
+    }
+    return NVFP4_OK;
 }
 
 typedef void (*GemmKernel)(GemmParams);
@@ -1211,6 +1328,9 @@ GemvParams make_params(const uint8_t *Wq, const uint8_t *Wscale, float gscale, c
     p.start2 = N;
     p.off0 = p.off1 = p.off2 = 0;
     p.ldy = N;
+    p.tp = p.T;
+    p.wpp = 1;
+    p.P = nullptr;
     return p;
 }
 
@@ -1359,6 +1479,47 @@ int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uin
     return launch_gemv(make_params(Wq, Wscale, gscale, X, Y, n, N, K), (hipStream_t)stream);
 }
 
+int nvfp4_gemv_kparts(int N, int K)
+{
+    if (N < 1 || K < 1)
+        return -NVFP4_ERR_RANGE;
+    if (K % 16 != 0 || K > kMaxK)
+        return -NVFP4_ERR_SHAPE;
+    return ksplit_for(N, K);
+}
+
+size_t nvfp4_gemv_workspace_bytes(int n, int N, int K, int ks)
+{
+    if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1 || K % 16 != 0 || K > kMaxK || ks < 0)
+        return 0;
+    return ksplit_workspace_bytes(ks == 0 ? ksplit_for(N, K) : ks, n, N);
+}
+
+int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X, uint16_t *Y,
+                  int n, int N, int K, int ks, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = validate_common(Wq, Wscale, X, Y, n, N, K);
+    if (st != NVFP4_OK)
+        return st;
+    if (ks < 0 || ks > kMaxKParts)
+        return NVFP4_ERR_RANGE;
+    if (ks == 0)
+        ks = ksplit_for(N, K);
+    const int T = (K + kTileK - 1) / kTileK;
+    const int tp = (T + ks - 1) / ks;
+    if (ks > T || (long long)(ks - 1) * tp >= T)
+        return NVFP4_ERR_SHAPE;   // some K part would be empty
+    if (ks > 1 && tp > kWaves * kMaxTilesPerWave)
+        return NVFP4_ERR_SHAPE;   // a K part longer than one pass (8192 columns)
+    if (ks > 1) {
+        if (!workspace || workspace_bytes < ksplit_workspace_bytes(ks, n, N))
+            return NVFP4_ERR_WORKSPACE;
+        if (!aligned(workspace, 16))
+            return NVFP4_ERR_ALIGN;
+    }
+    return launch_gemv(make_params(Wq, Wscale, gscale, X, Y, n, N, K), (hipStream_t)stream, ks, workspace);
+}
+
 int nvfp4_gemv_qkv(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
                    uint16_t *Y, int n, int K, const int32_t rows[3], const int64_t out_off[3],
                    int64_t ldy, void *stream)
@@ -1502,7 +1663,7 @@ int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves, int 
         return NVFP4_ERR_SHAPE;
     int cus = 256;   // MI355X; the launch itself uses the queried count
     Geometry geo;
-    if (!geometry_for(N, K, cus, &geo))
+    if (!geometry_for(N, K, cus, 1, &geo))
         return NVFP4_ERR_SHAPE;
     *workgroups = geo.workgroups;
     *waves = kWaves;
@@ -1544,6 +1705,7 @@ const char *nvfp4_strerror(int status)
     case NVFP4_ERR_SCHEDULE: return "invalid tile schedule";
     case NVFP4_ERR_LAUNCH: return "kernel launch failed";
     case NVFP4_ERR_DEVICE: return "current device is not gfx950";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
     }
 }

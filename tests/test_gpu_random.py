@@ -3,7 +3,8 @@ oracle element by element (same bar as the fixed cases: |y - y_ref| <= 1e-3 *
 sum_k |w x| + one bf16 ulp of y_ref).  The shapes are drawn so that most of
 them are ragged: N not a multiple of 16, K not a multiple of 128 (down to
 K = 16), K beyond one 8192-column chunk, odd token counts, and for the fused
-QKV entry random projection splits and output offsets."""
+QKV entry random projection splits and output offsets; the K-part entry at
+the library's part count and at a random valid one."""
 import numpy as np
 import pytest
 import torch
@@ -68,6 +69,14 @@ def test_random_gemv_and_gemm(N, K, seed):
     Yref, Aref = O.gemv(codes, scales, g, X)
     check(y_bits(nv.gemv(pw, x_to_dev(X[:n]))), Yref[:n], Aref[:n], "gemv %dx%d n=%d" % (N, K, n))
     check(y_bits(nv.gemm(pw, x_to_dev(X))), Yref, Aref, "gemm %dx%d n=%d" % (N, K, n_big))
+    # K parts: the library's choice, and a random valid part count
+    T = -(-K // 128)
+    valid = [k for k in range(1, min(T, 64) + 1)
+             if (k - 1) * -(-T // k) < T and (k == 1 or -(-T // k) <= 64)]
+    ks = int(valid[int(rng.integers(0, len(valid)))])
+    for k in (0, ks):
+        check(y_bits(nv.gemv_ws(pw, x_to_dev(X[:n]), k)), Yref[:n], Aref[:n],
+              "gemv_ws %dx%d n=%d ks=%d" % (N, K, n, k))
 
 
 @pytest.mark.parametrize("seed", list(range(8)))

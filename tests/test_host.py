@@ -60,6 +60,49 @@ def test_launch_geometry_fills_the_chip():
     assert wg == 3 and waves * tpw >= 2
 
 
+def _kparts_by_definition(N, K):
+    # K parts by the stated rule: one while the 128-column tiles fit one pass
+    # (64 tiles); beyond, the count (at most 64, no empty part, at most 64
+    # tiles per part) minimising ceil(ks * row_groups / 256) * tiles_per_part,
+    # the fewest on a tie
+    T = -(-K // 128)
+    RG = -(-N // 16)
+    if T <= 64:
+        return 1
+    best = None
+    for ks in range(2, min(T, 64) + 1):
+        tp = -(-T // ks)
+        if (ks - 1) * tp >= T or tp > 64:
+            continue
+        cost = -(-(ks * RG) // 256) * tp
+        if best is None or cost < best[0]:
+            best = (cost, ks)
+    return best[1]
+
+
+def test_kparts_policy():
+    assert nv.gemv_kparts(5120, 17408) == 4          # dense FFN down: 4 parts of 34 tiles, 5 rounds
+    for N, K in [(14336, 5120), (16384, 5120), (5120, 6144), (1024, 1024), (2048, 8192), (37, 144)]:
+        assert nv.gemv_kparts(N, K) == 1             # one pass: never split
+    assert nv.gemv_kparts(40, 1 << 18) == 64
+    for N in (1, 16, 100, 333, 5120, 8192, 40000):
+        for K in (8208, 9216, 12304, 17408, 28672, 40000, 1 << 18):
+            assert nv.gemv_kparts(N, K) == _kparts_by_definition(N, K), (N, K)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.gemv_kparts(16, 40)
+    with pytest.raises(nv.Nvfp4Error):
+        nv.gemv_kparts(0, 16)
+
+
+def test_workspace_bytes():
+    assert nv.gemv_workspace_bytes(16, 5120, 17408) == 4 * 16 * 5120 * 4
+    assert nv.gemv_workspace_bytes(3, 5120, 17408, 2) == 2 * 3 * 5120 * 4
+    assert nv.gemv_workspace_bytes(16, 14336, 5120) == 0      # policy: one part
+    assert nv.gemv_workspace_bytes(16, 5120, 17408, 1) == 0
+    assert nv.gemv_workspace_bytes(17, 5120, 17408) == 0      # invalid n
+    assert nv.gemv_workspace_bytes(1, 5120, 17400) == 0       # invalid K
+
+
 def test_byte_model_matches_the_pages(golden):
     b = golden["byte_model"]
     assert metrics.algorithmic_bytes(b["n"], b["N"], b["K"]) == b["bytes"]
@@ -85,6 +128,26 @@ FAKE = 0x100000   # 16-byte aligned, never dereferenced: every case below fails 
 ])
 def test_gemv_validation(args, status):
     assert nv.lib().nvfp4_gemv(*args, None) == status
+
+
+WS = (FAKE, FAKE, 1.0, FAKE, FAKE)
+
+
+@pytest.mark.parametrize("tail,status", [
+    ((1, 16, 17408, 4, 0, 1 << 20), 8),                 # null workspace
+    ((1, 16, 17408, 4, FAKE, 4 * 16 * 4 - 4), 8),       # workspace one float short
+    ((2, 5120, 17408, 0, FAKE, 4 * 2 * 5120 * 4 - 1), 8),  # policy (4 parts) needs more
+    ((1, 16, 17408, 4, FAKE + 8, 1 << 20), 3),          # workspace misaligned
+    ((1, 16, 17408, -1, FAKE, 1 << 20), 2),             # ks < 0
+    ((1, 16, 17408, 65, FAKE, 1 << 20), 2),             # ks beyond 64
+    ((1, 16, 256, 3, FAKE, 1 << 20), 4),                # 2 tiles: a third part would be empty
+    ((1, 16, 1152, 4, FAKE, 1 << 20), 4),               # 9 tiles in parts of 3: the 4th would be empty
+    ((1, 16, 17408, 2, FAKE, 1 << 20), 4),              # 68 tiles per part: longer than one pass
+    ((0, 16, 17408, 4, FAKE, 1 << 20), 2),              # n = 0
+    ((1, 16, 17400, 4, FAKE, 1 << 20), 4),              # K % 16
+])
+def test_gemv_ws_validation(tail, status):
+    assert nv.lib().nvfp4_gemv_ws(*WS, *tail, None) == status
 
 
 @pytest.mark.parametrize("args,status", [
