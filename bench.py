@@ -49,6 +49,7 @@ SHAPES = {
     "fused_qkv_14336x5120": (14336, 5120),
     "ssm_qkvz_16384x5120": (16384, 5120),
     "ssm_out_proj_5120x6144": (5120, 6144),
+    "dense_ffn_down_5120x17408": (5120, 17408),
     "smoke_1024x1024": (1024, 1024),
 }
 QKV_ROWS = (8192, 3072, 3072)
@@ -358,15 +359,16 @@ def cpu_baseline(N, K, n, seconds):
     }
 
 
-def stored_traffic():
+def stored_traffic(workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
-    or None if the summary is absent or was taken on a different kernel."""
+    or None if the summary is absent, covers another workload or was taken on
+    a different kernel."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha256_16") != kernel_source_hash():
+    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != workload:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -416,9 +418,17 @@ def main():
     rot = Rotation(nv, torch, N, K, seed=1100)
     log("rotation: %d copies, %.2f GiB" % (rot.count, rot.count * metrics.weight_bytes(N, K) / 2**30))
 
+    # Long-K shapes run in K parts (nvfp4_gemv_ws, workspace allocated once,
+    # outside the captured graphs); the others in one launch.
+    ks = 1 if qkv else nv.gemv_kparts(N, K)
     if qkv:
         def call(w, X, Y):
             nv.gemv_qkv(w, X, QKV_ROWS, QKV_OFFS, N, out=Y)
+    elif ks > 1:
+        ws = torch.empty(nv.gemv_workspace_bytes(16, N, K, ks), dtype=torch.uint8, device="cuda")
+
+        def call(w, X, Y):
+            nv.gemv_ws(w, X, ks, ws, out=Y)
     else:
         def call(w, X, Y):
             nv.gemv(w, X, out=Y)
@@ -469,7 +479,9 @@ def main():
         "data": "synthetic: W ~ N(0,0.02) fp32 quantised on the GPU, x ~ N(0,1) bf16; %d distinct weight copies rotated (%.2f GiB, cold against the 256 MB Infinity Cache)" % (rot.count, rot.count * wb / 2**30),
         "config": {"workload": args.workload, "N": N, "K": K, "n_tokens": n,
                    "qkv_rows": list(QKV_ROWS) if qkv else None,
-                   "launch": {"workgroups": wg, "waves_per_workgroup": waves, "tiles_per_wave": tpw},
+                   "launch": ({"workgroups": wg, "waves_per_workgroup": waves, "tiles_per_wave": tpw}
+                              if ks == 1 else {"k_parts": ks, "entry": "nvfp4_gemv_ws",
+                                               "launches": "K-part GEMV + nvfp4_ksplit_reduce_kernel"}),
                    "timing": "%d replays of a HIP graph of %d back-to-back launches, HIP events on the launch stream, after %.0f ms of untimed settle replays and %d warm-up steps" % (args.steps // L, L, SETTLE_S * 1e3, args.warmup)},
         "frac_hbm_peak": round(value / metrics.HBM_PEAK_GBPS, 4),
         "gemv_tokens_per_s": round(n / t_call, 1),
@@ -480,8 +492,9 @@ def main():
             "peak": metrics.HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ab / t_call / 1e9 / metrics.HBM_PEAK_GBPS, 4),
-            "traffic": stored_traffic(),
-            "kernel": "nvfp4_gemv_kernel<%d,%d,%s>" % (tpw, (n + 3) // 4, "true" if K % 128 == 0 else "false"),
+            "traffic": stored_traffic("%s n=%d" % (args.workload, n)),
+            "kernel": ("nvfp4_gemv_kernel<%d,%d,%s,false,false>" % (tpw, (n + 3) // 4, "true" if K % 128 == 0 else "false")
+                       if ks == 1 else "nvfp4_gemv_kernel<..., SPLIT> + nvfp4_ksplit_reduce_kernel"),
             "algorithmic_bytes_per_launch": ab,
         },
     }

@@ -490,19 +490,31 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
 
 // K-split epilogue: Y[t][r] = bf16_RNE(gscale * (((P[0] + P[1]) + P[2]) + ...)),
 // the K parts added in part order, so a token's result depends only on
-// (N, K, ks), never on n.  One thread per output, written at its projection's
-// offset as in the single-launch epilogue.
+// (N, K, ks), never on n.  Grid (ceil(N / 256), n): one thread per output,
+// written at its projection's offset as in the single-launch epilogue.  The
+// parts are loaded kReduceBatch at a time, all of a batch in flight together
+// (a dependent load per part would pay one memory latency per part).
+constexpr int kReduceBatch = 8;
+
 __global__ __launch_bounds__(256) void nvfp4_ksplit_reduce_kernel(GemvParams p, int ks)
 {
-    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;   // t * N + r
-    const long long count = (long long)p.n * p.N;
-    if (e >= count)
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    const int t = blockIdx.y;
+    if (r >= p.N)
         return;
-    const int t = (int)(e / p.N);
-    const int r = (int)(e - (long long)t * p.N);
-    float s = p.P[e];
-    for (int q = 1; q < ks; ++q)
-        s = s + p.P[q * count + e];
+    const long long count = (long long)p.n * p.N;
+    const float *src = p.P + (long long)t * p.N + r;
+    float s = 0.f;
+    for (int q0 = 0; q0 < ks; q0 += kReduceBatch) {
+        float v[kReduceBatch];
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j)
+            v[j] = q0 + j < ks ? __builtin_nontemporal_load(src + (q0 + j) * count) : 0.f;
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j)
+            if (q0 + j < ks)
+                s = (q0 + j == 0) ? v[j] : s + v[j];
+    }
     long long off;
     if (r >= p.start2)
         off = p.off2 + (r - p.start2);
@@ -1237,9 +1249,8 @@ int launch_gemv(const GemvParams &p, hipStream_t stream, int ks = 1, void *ws = 
     if (hipGetLastError() != hipSuccess)
         return NVFP4_ERR_LAUNCH;
     if (ks > 1) {
-        const long long count = (long long)p.n * p.N;
-        hipLaunchKernelGGL(nvfp4_ksplit_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                           stream, q, ks);
+        hipLaunchKernelGGL(nvfp4_ksplit_reduce_kernel, dim3((unsigned)((p.N + 255) / 256), (unsigned)p.n),
+                           dim3(256), 0, stream, q, ks);
         if (hipGetLastError() != hipSuccess)
             return NVFP4_ERR_LAUNCH;
     }
