@@ -594,7 +594,7 @@ constexpr int gemm_prefetch()
     return BMB == 2 ? 8 : (BMB == 4 ? 6 : 3);
 }
 
-// One workgroup: 4 waves x RGW row groups (64*RGW weight rows) times a tile of
+// One workgroup: GW waves x RGW row groups (16*GW*RGW weight rows) times a tile of
 // BM = 16*BMB tokens.  Per 128-column K step the workgroup stages the token
 // tile's X slice in LDS (double-buffered), each wave converts its RGW code
 // tiles to bf16 operands and runs 4 * RGW * BMB MFMAs.  The loads of step
@@ -682,26 +682,6 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
         for (int tb = 0; tb < BMB; ++tb)
             acc[r][tb] = zero;
 
-    // One K step from LDS buffer `buf` and weight slot q.
-    auto compute_plain = [&](auto slot_c, int buf) {
-        constexpr int q = decltype(slot_c)::value;
-        const char *xb = xs[buf] + i * kXRow + 16 * g;
-        static_for<4>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            bf16x8 bop[RGW];
-#pragma unroll
-            for (int r = 0; r < RGW; ++r)
-                bop[r] = __builtin_bit_cast(bf16x8, dequant_pair<(j & 1) != 0>(cw[q][r][j], sw[q][r][j >> 1]));
-#pragma unroll
-            for (int tb = 0; tb < BMB; ++tb) {
-                const bf16x8 aop = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow + 64 * j);
-#pragma unroll
-                for (int r = 0; r < RGW; ++r)
-                    acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[r], acc[r][tb], 0, 0, 0);
-            }
-        });
-    };
-
     // One K step from LDS buffer `buf` and weight slot q, software-pipelined
     // over its four 32-column substeps: the A fragments and the dequantised B
     // operands of substep j+1 are produced while substep j's MFMAs run.
@@ -735,15 +715,8 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
         });
     };
 
-    // The pipelined form needs two more A and B register sets; with two row
-    // groups per wave that would drop the kernel to one wave per SIMD, which
-    // measured slower than the plain form.
-    auto compute = [&](auto slot_c, int buf) {
-        if constexpr (RGW == 1 || GW == 8)
-            compute_pipe(slot_c, buf);
-        else
-            compute_plain(slot_c, buf);
-    };
+    static_assert(RGW == 1 || GW == 8, "row tiles: 4 waves x 1 row group or 8 waves x 2");
+    auto compute = [&](auto slot_c, int buf) { compute_pipe(slot_c, buf); };
 
     static_for<P>([&](auto qc) { issue(qc, decltype(qc)::value); });
     land(std::integral_constant<int, 0>{}, 0);
@@ -1266,27 +1239,25 @@ struct GemmGeometry {
 
 // Tile shape of the prefill GEMM for n tokens of an N x K weight on `cus`
 // compute units.  The token tile is the smallest of 32 / 64 / 128 tokens that
-// holds n (capped at 128).  The row tile is the largest of 256 rows (8 waves x
-// 2 row groups), 128 rows (4 x 2) and 64 rows (4 x 1) that still gives every
-// compute unit a workgroup (narrower tiles for grids that would under-fill
-// the chip; larger tiles read X fewer times per flop).
+// holds n (capped at 128).  The row tile is 256 rows (8 waves x 2 row groups,
+// one workgroup per compute unit), which shares each X tile among the most
+// rows and measured the fastest per row, once its grid gives at least half
+// the compute units a workgroup; below that, 64 rows (4 waves x 1 row group,
+// two workgroups per compute unit), whose four times as many workgroups keep
+// the longest one's work shorter.  A 128-row tile (4 x 2) never won: above the
+// threshold it puts two workgroups on some compute unit, as long a critical
+// path at a lower rate per row (fused QKV, n = 320 .. 512: 90 .. 97 us against
+// 74 .. 82 us for 256 rows), below it the 64-row tile was as fast or faster.
 void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
 {
     geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
     const int bm = 16 * geo->bmb;
     const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
     geo->grid_y = (n + bm - 1) / bm;
-    static const int shapes[3][2] = {{2, 8}, {2, 4}, {1, 4}};   // (row groups per wave, waves)
-    int pick = 2;
-    for (int j = 0; j < 3; ++j) {
-        const long long tiles = (RG + shapes[j][0] * shapes[j][1] - 1) / (shapes[j][0] * shapes[j][1]);
-        if (tiles * geo->grid_y >= cus) {
-            pick = j;
-            break;
-        }
-    }
-    geo->rgw = shapes[pick][0];
-    geo->gw = shapes[pick][1];
+    const long long tiles256 = (RG + 15) / 16;
+    const bool wide = tiles256 * geo->grid_y * 2 >= cus;
+    geo->rgw = wide ? 2 : 1;
+    geo->gw = wide ? 8 : 4;
     geo->grid_x = (int)((RG + geo->rgw * geo->gw - 1) / (geo->rgw * geo->gw));
 }
 
@@ -1303,7 +1274,7 @@ GemmKernel pick_gemm_bmb(int bmb)
 GemmKernel pick_gemm(const GemmGeometry &geo)
 {
     if (geo.rgw == 2)
-        return geo.gw == 8 ? pick_gemm_bmb<2, 8>(geo.bmb) : pick_gemm_bmb<2, 4>(geo.bmb);
+        return pick_gemm_bmb<2, 8>(geo.bmb);
     return pick_gemm_bmb<1, 4>(geo.bmb);
 }
 

@@ -172,16 +172,25 @@ def test_gemm_geometry_rule():
     assert nv.gemm_geometry(64, 14336, 5120)[1] == 64
     assert nv.gemm_geometry(65, 14336, 5120)[1] == 128
     assert nv.gemm_geometry(1000, 14336, 5120)[1] == 128
-    # 896 row groups: 128-row tiles give 112 x 1 workgroups at n = 128, which
-    # would leave the chip under-filled, so the narrow 64-row tile is used
-    assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)
-    # with 4 token tiles the 256-row tile would give 224 workgroups, the
-    # 128-row tile 448: the largest tile that fills the chip wins
-    assert nv.gemm_geometry(512, 14336, 5120) == (128, 128, 112, 4)
-    # with 8 token tiles the 256-row tile (8 waves) already fills it
-    assert nv.gemm_geometry(1024, 14336, 5120) == (256, 128, 56, 8)
-    r, t, gx, gy = nv.gemm_geometry(300, 37, 144)    # ragged: 3 row groups, 3 token tiles
-    assert gx * r >= 37 and gy * t >= 300
+    # row tile: 256 rows (8 waves) once its grid gives at least half of the
+    # 256 compute units a workgroup, else 64 rows (4 waves, two per unit).
+    # Fused QKV, 896 row groups = 56 tiles of 256 rows:
+    assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)     # 56 workgroups: under half
+    assert nv.gemm_geometry(256, 14336, 5120) == (64, 128, 224, 2)     # 112: under half
+    assert nv.gemm_geometry(320, 14336, 5120) == (256, 128, 56, 3)     # 168
+    assert nv.gemm_geometry(512, 14336, 5120) == (256, 128, 56, 4)     # 224
+    assert nv.gemm_geometry(1024, 14336, 5120) == (256, 128, 56, 8)    # 448
+    # 16384 rows, 2 token tiles: 128 workgroups of 256 rows is exactly half
+    assert nv.gemm_geometry(256, 16384, 5120) == (256, 128, 64, 2)
+    assert nv.gemm_geometry(128, 16384, 5120) == (64, 128, 256, 1)
+    # 5120 rows (20 tiles of 256 rows): 7 token tiles give 140 workgroups, 6 give 120
+    assert nv.gemm_geometry(896, 5120, 6144) == (256, 128, 20, 7)
+    assert nv.gemm_geometry(768, 5120, 6144) == (64, 128, 80, 6)
+    # 34816 rows (136 tiles): the 256-row tile is wide enough at one token tile
+    assert nv.gemm_geometry(40, 34816, 5120) == (256, 64, 136, 1)
+    for n, N in ((17, 1), (300, 37), (5000, 100), (1 << 20, 16)):
+        r, t, gx, gy = nv.gemm_geometry(n, N, 144)
+        assert r in (64, 256) and gx * r >= N and gy * t >= n and (gx - 1) * r < N
     with pytest.raises(nv.Nvfp4Error):
         nv.gemm_geometry(0, 16, 16)
 
