@@ -347,15 +347,32 @@ def cpu_baseline(N, K, n, seconds):
         if time.perf_counter() - t_start >= seconds and len(times) >= 2:
             break
     t = float(np.median(times))
+    cores = O.num_threads()
+    # The same call on one thread: a warm-up and the median of 3.
+    t1s = []
+    for _ in range(4):
+        t0 = time.perf_counter()
+        O.gemv(codes, scales, g, X, nthreads=1)
+        t1s.append(time.perf_counter() - t0)
+    t1 = float(np.median(t1s[1:]))
     wb = metrics.weight_bytes(N, K)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(wb / t / 1e9, 4),
         "unit": "effective weight GB/s",
         "gemv_tokens_per_s": round(n / t, 2),
-        "cores": O.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": "full %dx%d NVFP4 weight, n=%d tokens, %d runs, median %.3f s per call"
                   % (N, K, n, len(times), t),
+        "single_thread": {"value": round(wb / t1 / 1e9, 4), "gemv_tokens_per_s": round(n / t1, 2),
+                          "sample": "same call, median of 3 after a warm-up, %.3f s per call" % t1},
+        "host": {"cpu_model": cpu_model, "os_cpu_count": os.cpu_count()},
     }
 
 
@@ -459,6 +476,19 @@ def main():
     t_host = time.perf_counter() - t_host0
     elapsed = e0.elapsed_time(e1) * 1e-3
     t_call = elapsed / args.steps
+    # Spread of the per-call time across replays: a second pass of the same
+    # replays with an event after each, outside the timed region.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps // L + 1)]
+    marks[0].record(s)
+    for ev in marks[1:]:
+        gt.replay()
+        ev.record(s)
+    torch.cuda.synchronize()
+    per_replay = sorted(a.elapsed_time(b) * 1e3 / L for a, b in zip(marks[:-1], marks[1:]))
+
+    def pct(q):
+        return round(per_replay[min(len(per_replay) - 1, int(q * len(per_replay)))], 3)
+
 
     wb = metrics.weight_bytes(N, K)
     ab = metrics.algorithmic_bytes(n, N, K)
@@ -486,6 +516,9 @@ def main():
         "frac_hbm_peak": round(value / metrics.HBM_PEAK_GBPS, 4),
         "gemv_tokens_per_s": round(n / t_call, 1),
         "host_wall_s_timed_region": round(t_host, 6),
+        "per_call_us_over_replays": {"replays": len(per_replay), "launches_per_replay": L,
+                                     "p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                                     "pass": "after the timed region, one event per replay"},
         "roofline": {
             "bound": "hbm",
             "achieved": round(ab / t_call / 1e9, 1),

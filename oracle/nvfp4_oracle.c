@@ -242,12 +242,15 @@ void oracle_gemv(const uint8_t *codes, const uint8_t *scales, float gscale,
                  int nthreads)
 {
     e4m3_fill();
-    (void)nthreads;
+    /* nthreads > 0 sets this call's thread count only (a clause on the
+       region, not the process-wide setting). */
 #ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    const int nt = 1;
+    (void)nthreads;
 #endif
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(nt)
     for (int r = 0; r < N; ++r) {
         for (int t = 0; t < n; ++t) {
             double acc = 0.0, mag = 0.0;

@@ -365,3 +365,14 @@ def test_qkv_scatter():
     Y = np.arange(2 * 4, dtype=np.float64).reshape(2, 4)
     out = O.qkv_scatter(Y, (2, 1, 1), (0, 3, 5), ldy=7, fill=-1.0)
     assert out.tolist() == [[0, 1, -1, 2, -1, 3, -1], [4, 5, -1, 6, -1, 7, -1]]
+
+
+def test_thread_count_argument_is_per_call():
+    """A one-thread oracle call leaves later default calls and the reported
+    thread count alone (no process-wide OpenMP setting)."""
+    before = O.num_threads()
+    codes = np.zeros((16, 8), dtype=np.uint8)
+    scales = np.full((16, 1), 0x38, dtype=np.uint8)
+    X = np.zeros((1, 16), dtype=np.uint16)
+    O.gemv(codes, scales, 1.0, X, nthreads=1)
+    assert O.num_threads() == before
