@@ -329,6 +329,34 @@ def decode_step(nv, torch, n=16):
             "timing": "20 replays of a HIP graph of the 64 launches of one step"}
 
 
+def arith_rate(nv, torch, blocks=8192, reps=5):
+    """Per-block arithmetic rate of the MFMA and VALU forms (nvfp4_block_rate,
+    register data on every SIMD, two waves each), and what it implies for the
+    fused QKV at one launch: each SIMD runs two waves of 4 row groups x 5 tiles
+    x 8 blocks = 160 blocks each."""
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, path in (("mfma", nv.RATE_MFMA), ("valu", nv.RATE_VALU)):
+        out[name] = {}
+        for n in (1, 4, 8, 16):
+            nv.block_rate(path, n, blocks, sink)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                nv.block_rate(path, n, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            ns = t / blocks * 1e9
+            out[name][str(n)] = {"ns_per_block_two_waves_per_simd": round(ns, 3),
+                                 "fused_qkv_compute_only_us": round(160 * ns * 1e-3, 3)}
+    out["what"] = ("time of one 16-element block of a 16-row group on every SIMD, two waves at once, "
+                   "arithmetic only (no loads); fused QKV needs 160 such blocks per SIMD per launch")
+    return out
+
+
 def cpu_baseline(N, K, n, seconds):
     """The oracle (fp64, OpenMP over rows) on the same workload shape: the
     whole N x K weight for n tokens, repeated until `seconds` of CPU time."""
@@ -407,6 +435,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed region (for rocprofv3 runs): no sweep, no CPU baseline")
+    ap.add_argument("--arith-only", action="store_true",
+                    help="run only the MFMA-vs-VALU arithmetic-rate probe (nvfp4_block_rate) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -426,6 +456,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         print(json.dumps(copy_calibration(torch)), flush=True)
+        return
+    if args.arith_only:
+        print(json.dumps({"arith_rate": arith_rate(nv, torch)}), flush=True)
         return
     N, K = SHAPES[args.workload]
     n = args.n
@@ -626,6 +659,9 @@ def main():
             del re_
             torch.cuda.empty_cache()
         result["extra_shapes"] = extra
+
+        log("MFMA vs VALU arithmetic rate ...")
+        result["arith_rate"] = arith_rate(nv, torch)
 
         log("prefill GEMM sweep ...")
         result["prefill_fused_qkv"] = prefill_sweep(nv, torch, t_call)

@@ -221,6 +221,29 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
 int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup,
                         int *tokens_per_workgroup, int *grid_x, int *grid_y);
 
+/* Paths of nvfp4_block_rate. */
+#define NVFP4_RATE_MFMA 0
+#define NVFP4_RATE_VALU 1
+
+/* Measurement aid, not part of the GEMV path: the issue rate of the
+ * arithmetic for one 16-element block of a 16-row group times n tokens, on
+ * register data (no memory traffic), for the two ways to do it on gfx950.
+ * NVFP4_RATE_MFMA is nvfp4_gemv's sequence (two fp4->bf16 converts, one
+ * 16x16x16 bf16 MFMA with the tokens as M, ceil(n/4) scale FMAs);
+ * NVFP4_RATE_VALU the best VALU form found (the same converts, then per token
+ * an LDS read of its 4 activations, two v_dot2_f32_bf16 and one scale FMA).
+ * This is the measurement behind choosing MFMA for n = 1..16 (the pages'
+ * kernels are VALU/tensor-core designs for another GPU).  Runs 256 workgroups
+ * of 8 waves (two per SIMD), each wave `blocks` blocks (rounded down to a
+ * multiple of 8, with independent codes per block as loaded tiles have); the
+ * time of the launch divided by that count is the time of one block on every
+ * SIMD of the chip, two waves at once.  n in {1, 2, 4, 8, 12, 16}.  sink:
+ * DEVICE, at least 256*512*4 bytes, 4-byte aligned, receives meaningless
+ * values.  Errors: NULL, RANGE (path, n, blocks < 8, sink_bytes), ALIGN,
+ * LAUNCH. */
+int nvfp4_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes,
+                     void *stream);
+
 /* Measurement aid, not part of the GEMV path: reads `bytes` bytes of `buf`
  * (DEVICE, 16-byte aligned, bytes a positive multiple of 16) once with the
  * streaming pattern that reads fastest on MI355X (1024-thread workgroups,

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.nvfp4_read_stream.restype = _i32
         L.nvfp4_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.nvfp4_block_rate.restype = _i32
+        L.nvfp4_block_rate.argtypes = [_i32, _i32, _i32, _vp, ctypes.c_size_t, _vp]
         L.nvfp4_strerror.restype = ctypes.c_char_p
         L.nvfp4_strerror.argtypes = [_i32]
         _lib = L
@@ -317,6 +319,17 @@ def gemm(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None
     _check(lib().nvfp4_gemm(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                             Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemm")
     return Y
+
+
+RATE_MFMA, RATE_VALU = 0, 1
+
+
+def block_rate(path: int, n: int, blocks: int, sink: torch.Tensor, stream=None) -> None:
+    """Launch the per-block arithmetic-rate probe (RATE_MFMA or RATE_VALU)
+    for n tokens; ``sink`` is a float32 device tensor of >= 256*512 elements."""
+    _dev(sink, torch.float32, "sink")
+    _check(lib().nvfp4_block_rate(int(path), int(n), int(blocks), sink.data_ptr(), sink.numel() * 4,
+                                  _stream(stream)), "nvfp4_block_rate")
 
 
 def read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -14,7 +14,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "nvfp4.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "nvfp4.hip"), os.path.join(PKG, "csrc", "block_rate.hip")]
 LIB = os.path.join(PKG, "libnvfp4.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,192 @@
+// Measurement aid, not part of the GEMV path: the issue rate of the two ways
+// to multiply one 16-element NVFP4 block of a 16-row group by n <= 16 decode
+// tokens on gfx950, on register data with no memory traffic.
+//
+//  * MFMA (what nvfp4_gemv does): two v_cvt_scalef32_pk_bf16_fp4 (4 codes of
+//    the lane's weight row -> exact bf16), one v_mfma_f32_16x16x16_bf16 with
+//    the tokens as M, then ceil(n/4) fp32 FMAs applying the E4M3 block scale
+//    (trailing the MFMA by two blocks), and one v_cvt_pk_f32_fp8 per two
+//    blocks for the scales.
+//  * VALU: the same conversions, then per token an 8-byte LDS read of the
+//    token's 4 activations at the lane's K positions (the activation rows of
+//    all n tokens cannot stay in registers), two v_dot2_f32_bf16 (4 MACs) and
+//    one FMA with the block scale.
+//
+// Both run 8 waves per workgroup (two per SIMD, the GEMV's occupancy) on 256
+// workgroups; each wave runs `blocks` blocks (rounded down to a multiple of
+// 8) in groups of 8.  Each lane holds 8 code words; block j of a group uses
+// word j XORed with the group's scalar counter (one VALU op, like a loaded
+// tile: no block depends on the previous one, nothing can be hoisted).  A
+// compiler barrier per group keeps the VALU path's LDS reads inside the loop.
+// The outputs only feed a sink.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "../../include/nvfp4.h"
+
+namespace {
+
+typedef unsigned int u32;
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kProbeWorkgroups = 256;
+constexpr int kProbeThreads = 512;
+
+__device__ __forceinline__ bf16x2 cvt_lo(u32 w) { return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0); }
+__device__ __forceinline__ bf16x2 cvt_hi(u32 w) { return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1); }
+
+template <typename F, int... J>
+__device__ __forceinline__ void unroll_impl(F &&f, std::integer_sequence<int, J...>)
+{
+    (f(std::integral_constant<int, J>{}), ...);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F &&f)
+{
+    unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int NT>
+__global__ __launch_bounds__(kProbeThreads) void block_rate_mfma_kernel(u32 seed, int blocks, float *sink)
+{
+    constexpr int NV = (NT + 3) / 4;
+    u32 wb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        wb[j] = (seed + (u32)j * 0x9E3779B9u) ^ (u32)(threadIdx.x * 2654435761u);
+    const u32x2 xa = {wb[0] * 3u, wb[1] * 5u};
+    const s16x4 aop = __builtin_bit_cast(s16x4, xa);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = zero, p1 = zero, p2 = zero;
+    float s1 = 0.f, s2 = 0.f;
+    for (int b0 = 0; b0 + 8 <= blocks; b0 += 8) {
+        float sc[2] = {1.f, 1.f};
+        unroll<8>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const u32 w = wb[j] ^ (u32)b0;
+            if constexpr ((j & 1) == 0) {
+                const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)(w & 0x3F3F3F3Fu), false);
+                sc[0] = f2[0];
+                sc[1] = f2[1];
+            }
+            const u32x2 bw = {__builtin_bit_cast(u32, cvt_lo(w)), __builtin_bit_cast(u32, cvt_hi(w))};
+            const f32x4 pr =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, __builtin_bit_cast(s16x4, bw), zero, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                acc[v] = __builtin_fmaf(s2, p2[v], acc[v]);
+            p2 = p1;
+            s2 = s1;
+            p1 = pr;
+            s1 = sc[j & 1];
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+        });
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        r += __builtin_fmaf(s1, p1[v], __builtin_fmaf(s2, p2[v], acc[v]));
+    sink[blockIdx.x * kProbeThreads + threadIdx.x] = r;
+}
+
+template <int NT>
+__global__ __launch_bounds__(kProbeThreads) void block_rate_valu_kernel(u32 seed, int blocks, float *sink)
+{
+    // Per wave: 8 blocks x 16 tokens x 16 columns of bf16 activations (4 KiB),
+    // read back as the lane's 4 columns of each token.
+    __shared__ u32x2 xs[kProbeThreads / 64][8][16][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    u32 wb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        wb[j] = (seed + (u32)j * 0x9E3779B9u) ^ (u32)(threadIdx.x * 2654435761u);
+    for (int e = lane; e < 8 * 16 * 4; e += 64)
+        xs[wave][e >> 6][(e >> 2) & 15][e & 3] = u32x2{wb[0] + (u32)e * 0x9E3779B9u, wb[1] ^ (u32)e};
+    __syncthreads();
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        acc[t] = 0.f;
+    for (int b0 = 0; b0 + 8 <= blocks; b0 += 8) {
+        float sc[2] = {1.f, 1.f};
+        asm volatile("" ::: "memory");
+        unroll<8>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const u32 w = wb[j] ^ (u32)b0;
+            if constexpr ((j & 1) == 0) {
+                const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)(w & 0x3F3F3F3Fu), false);
+                sc[0] = f2[0];
+                sc[1] = f2[1];
+            }
+            const bf16x2 lo = cvt_lo(w), hi = cvt_hi(w);
+            const float s = sc[j & 1];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x2 x = xs[wave][j][t][g];
+                // The words are copied to scalars first: __builtin_bit_cast of
+                // an ext-vector element reads element 0 with this compiler.
+                const u32 x0 = x[0], x1 = x[1];
+                float part = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2, x0), 0.f, false);
+                part = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, x1), part, false);
+                acc[t] = __builtin_fmaf(s, part, acc[t]);
+            }
+        });
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        r += acc[t];
+    sink[blockIdx.x * kProbeThreads + threadIdx.x] = r;
+}
+
+typedef void (*ProbeKernel)(u32, int, float *);
+
+template <int NT>
+ProbeKernel pick_probe(int path)
+{
+    return path == NVFP4_RATE_MFMA ? block_rate_mfma_kernel<NT> : block_rate_valu_kernel<NT>;
+}
+
+ProbeKernel pick_probe_n(int path, int n)
+{
+    switch (n) {
+    case 1: return pick_probe<1>(path);
+    case 2: return pick_probe<2>(path);
+    case 4: return pick_probe<4>(path);
+    case 8: return pick_probe<8>(path);
+    case 12: return pick_probe<12>(path);
+    default: return pick_probe<16>(path);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes, void *stream)
+{
+    if (!sink)
+        return NVFP4_ERR_NULL;
+    if ((path != NVFP4_RATE_MFMA && path != NVFP4_RATE_VALU) || blocks < 8 ||
+        (n != 1 && n != 2 && n != 4 && n != 8 && n != 12 && n != 16))
+        return NVFP4_ERR_RANGE;
+    if (sink_bytes < (size_t)kProbeWorkgroups * kProbeThreads * sizeof(float))
+        return NVFP4_ERR_RANGE;
+    if ((uintptr_t)sink % 4 != 0)
+        return NVFP4_ERR_ALIGN;
+    hipLaunchKernelGGL(pick_probe_n(path, n), dim3(kProbeWorkgroups), dim3(kProbeThreads), 0,
+                       (hipStream_t)stream, 0x1234567u, blocks, sink);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -313,6 +313,18 @@ def test_full_size_parity(name, N, K, cfg, zero_outlier, row_scale, n):
     assert_parity(Y, Yref, Aref, "%s n=%d" % (name, n))
 
 
+def test_block_rate_probe_runs():
+    """The MFMA-vs-VALU arithmetic-rate probe launches for every n it takes
+    and writes its sink (its values carry no meaning)."""
+    sink = torch.full((256 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    for path in (nv.RATE_MFMA, nv.RATE_VALU):
+        for n in (1, 2, 4, 8, 12, 16):
+            sink.fill_(float("nan"))
+            nv.block_rate(path, n, 64, sink)
+            torch.cuda.synchronize()
+            assert not bool(torch.isnan(sink).all()), (path, n)
+
+
 def test_read_stream_runs_and_leaves_data():
     """The read-ceiling aid reads a buffer without changing it (sink written
     only on a checksum value the data below cannot produce)."""

@@ -130,6 +130,18 @@ def test_gemv_validation(args, status):
     assert nv.lib().nvfp4_gemv(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, 16, 8, 0, 1 << 20), 1),                  # null sink
+    ((2, 16, 8, FAKE, 1 << 20), 2),               # unknown path
+    ((1, 3, 8, FAKE, 1 << 20), 2),                # n not one of 1, 2, 4, 8, 12, 16
+    ((0, 16, 7, FAKE, 1 << 20), 2),               # fewer than one group of 8 blocks
+    ((0, 16, 8, FAKE, 256 * 512 * 4 - 4), 2),     # sink one float short
+    ((1, 8, 8, FAKE + 2, 1 << 20), 3),            # sink misaligned
+])
+def test_block_rate_validation(args, status):
+    assert nv.lib().nvfp4_block_rate(*args, None) == status
+
+
 WS = (FAKE, FAKE, 1.0, FAKE, FAKE)
 
 
