@@ -71,6 +71,7 @@ PREFILL_N = [32, 64, 128, 256, 512, 1024, 2048]
 ROTATION_BYTES = 1 << 30
 SETTLE_S = 0.03
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_n16_counters.json")
+PER_N_COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_per_n_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_02_amd", "csrc", "nvfp4.hip")
 
 
@@ -404,6 +405,26 @@ def cpu_baseline(N, K, n, seconds):
     }
 
 
+def annotate_counter_bandwidth(sweep: dict, workload: str) -> None:
+    """Add the HBM bandwidth rocprofv3's FETCH_SIZE + WRITE_SIZE imply (bytes
+    per launch from the committed per-n counter summary / time per call) to
+    the sweep points it covers, while that summary matches the kernel source
+    and the workload."""
+    from nvfp4_weight_only_02_amd import metrics
+    try:
+        with open(PER_N_COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return
+    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != workload:
+        return
+    for n, b in c.get("hbm_bytes_per_launch", {}).items():
+        if n in sweep:
+            gbps = b / (sweep[n]["us"] * 1e-6) / 1e9
+            sweep[n]["hbm_GBps_counters"] = round(gbps, 1)
+            sweep[n]["frac_hbm_peak_counters"] = round(gbps / metrics.HBM_PEAK_GBPS, 4)
+
+
 def stored_traffic(workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None if the summary is absent, covers another workload or was taken on
@@ -579,6 +600,7 @@ def main():
     if n_list:
         log("per-n sweep %s ..." % args.workload)
         sweeps[args.workload] = sweep_shape(torch, rot, n_list, call, 2000)
+        annotate_counter_bandwidth(sweeps[args.workload], args.workload)
         if qkv:
             sweeps[args.workload + " (plain nvfp4_gemv)"] = sweep_shape(
                 torch, rot, n_list, lambda w, X, Y: nv.gemv(w, X, out=Y), 2000, warm=False)
