@@ -69,6 +69,18 @@ EXTRA_N = [1, 2, 4, 8, 16]
 # Prefill (many-token) GEMM sweep on the fused QKV weight.
 PREFILL_N = [32, 64, 128, 256, 512, 1024, 2048]
 ROTATION_BYTES = 1 << 30
+# The pages' own numbers, on another GPU and memory system (GB10, sm_121):
+# context for the reader, never a target and never the vs_baseline figure.
+PAGES_CONTEXT = {
+    "hardware": "GB10 (sm_121), CUDA kernels, as the pages report them",
+    "w4a16_tile_gemm_M16_us": {  # spark_model::layers page, measured decode-shape table
+        "ssm_qkvz_16384x5120": [272.4, 281.9, 341.6],
+        "fused_qkv_14336x5120": [262.8, 273.9, 328.5],
+        "ssm_out_proj_5120x6144": [163.3, 237.7, 240.7],
+        "stream_ceiling_GBps": 230},
+    "decode_tok_s_per_sequence_C4": {"wide_gemm": 15.8, "tiled_gemv": 26.7},  # Atlas PR #266, A/B table
+    "note": "different hardware and end-to-end serving numbers; no figure of the pages is this metric on MI355X",
+}
 SETTLE_S = 0.03
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_n16_counters.json")
 PER_N_COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_fused_qkv_14336x5120_per_n_counters.json")
@@ -569,6 +581,7 @@ def main():
                    "timing": "%d replays of a HIP graph of %d back-to-back launches, HIP events on the launch stream, after %.0f ms of untimed settle replays and %d warm-up steps" % (args.steps // L, L, SETTLE_S * 1e3, args.warmup)},
         "frac_hbm_peak": round(value / metrics.HBM_PEAK_GBPS, 4),
         "gemv_tokens_per_s": round(n / t_call, 1),
+        "context_pages": PAGES_CONTEXT,
         "host_wall_s_timed_region": round(t_host, 6),
         "per_call_us_over_replays": {"replays": len(per_replay), "launches_per_replay": L,
                                      "p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
