@@ -69,10 +69,15 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     lines = [line for line in res.stdout.splitlines()
              if "packed-fp32-ops' is not a recognized feature" not in line]
-    check_resources("\n".join(lines))
     out = "\n".join(line for line in lines if "remark:" not in line)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
+    try:
+        check_resources("\n".join(lines))
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + out)
+    except RuntimeError:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
