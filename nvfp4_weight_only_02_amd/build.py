@@ -69,7 +69,17 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     lines = [line for line in res.stdout.splitlines()
              if "packed-fp32-ops' is not a recognized feature" not in line]
-    out = "\n".join(line for line in lines if "remark:" not in line)
+    # Drop the resource remarks and the source lines clang quotes under them.
+    kept, after_remark = [], False
+    for line in lines:
+        if "remark:" in line:
+            after_remark = True
+            continue
+        if after_remark and re.match(r"^\s*(\d+\s*)?\|", line):
+            continue
+        after_remark = False
+        kept.append(line)
+    out = "\n".join(kept)
     try:
         check_resources("\n".join(lines))
         if res.returncode != 0:
