@@ -603,10 +603,12 @@ constexpr int gemm_prefetch()
 // traffic, so every step issues the same loads and every wait count is a
 // constant).  Each output's sum runs over K in the same order whatever n, the
 // tile shape or the token's place in its tile.
-template <int RGW, int BMB, int GW>
+template <int RGW, int BMB, int GW, int TS>
 __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
 {
     constexpr int BM = BMB * 16;
+    constexpr int WB = BMB / TS;   // token blocks per wave: TS waves share a row group's token tile
+    static_assert(BMB % TS == 0 && GW % TS == 0, "token split");
     constexpr int P = gemm_prefetch<BMB>();
     constexpr int L = 4 * BMB / GW + 2 * RGW;   // loads per step and thread
     static_assert((P - 1) * L <= 63, "vmcnt is a 6-bit field");
@@ -615,7 +617,8 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: buffer resources in SGPRs
     const int i = lane & 15, g = lane >> 4;
     constexpr int XL = 4 * BMB / GW;   // X chunks per thread and step
-    const int rgw0 = (blockIdx.x * GW + wave) * RGW;   // first row group of this wave
+    const int wtb0 = (wave % TS) * WB;                              // first token block of this wave
+    const int rgw0 = (blockIdx.x * (GW / TS) + wave / TS) * RGW;   // first row group of this wave
     const int tok0 = blockIdx.y * BM;
     const int ntok = min(BM, p.n - tok0);
     const int nrg = max(0, min(RGW, p.RG - rgw0));
@@ -675,11 +678,11 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
     };
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[RGW][BMB];
+    f32x4 acc[RGW][WB];
 #pragma unroll
     for (int r = 0; r < RGW; ++r)
 #pragma unroll
-        for (int tb = 0; tb < BMB; ++tb)
+        for (int tb = 0; tb < WB; ++tb)
             acc[r][tb] = zero;
 
     // One K step from LDS buffer `buf` and weight slot q, software-pipelined
@@ -687,10 +690,10 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
     // operands of substep j+1 are produced while substep j's MFMAs run.
     auto compute_pipe = [&](auto slot_c, int buf) {
         constexpr int q = decltype(slot_c)::value;
-        const char *xb = xs[buf] + i * kXRow + 16 * g;
-        bf16x8 a[2][BMB], b[2][RGW];
+        const char *xb = xs[buf] + (wtb0 * 16 + i) * kXRow + 16 * g;
+        bf16x8 a[2][WB], b[2][RGW];
 #pragma unroll
-        for (int tb = 0; tb < BMB; ++tb)
+        for (int tb = 0; tb < WB; ++tb)
             a[0][tb] = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow);
 #pragma unroll
         for (int r = 0; r < RGW; ++r)
@@ -700,14 +703,14 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
             constexpr int cur = j & 1, nxt = cur ^ 1;
             if constexpr (j < 3) {
 #pragma unroll
-                for (int tb = 0; tb < BMB; ++tb)
+                for (int tb = 0; tb < WB; ++tb)
                     a[nxt][tb] = *reinterpret_cast<const bf16x8 *>(xb + tb * 16 * kXRow + 64 * (j + 1));
 #pragma unroll
                 for (int r = 0; r < RGW; ++r)
                     b[nxt][r] = __builtin_bit_cast(bf16x8, dequant_pair<((j + 1) & 1) != 0>(cw[q][r][j + 1], sw[q][r][(j + 1) >> 1]));
             }
 #pragma unroll
-            for (int tb = 0; tb < BMB; ++tb)
+            for (int tb = 0; tb < WB; ++tb)
 #pragma unroll
                 for (int r = 0; r < RGW; ++r)
                     acc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][tb], b[cur][r], acc[r][tb], 0, 0, 0);
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
         });
     };
 
-    static_assert(RGW == 1 || GW == 8, "row tiles: 4 waves x 1 row group or 8 waves x 2");
+    static_assert(RGW == 1 || GW == 8, "row tiles: 1 row group per wave, or 8 waves x 2");
     auto compute = [&](auto slot_c, int buf) { compute_pipe(slot_c, buf); };
 
     static_for<P>([&](auto qc) { issue(qc, decltype(qc)::value); });
@@ -735,18 +738,18 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's trailing loads read nothing
 
-    // Component v of lane (g, i) of acc[r][tb]: token tok0 + 16*tb + 4*g + v,
-    // weight row 16*(rgw0 + r) + i.
+    // Component v of lane (g, i) of acc[r][tb]: token tok0 + 16*(wtb0 + tb) +
+    // 4*g + v, weight row 16*(rgw0 + r) + i.
 #pragma unroll
     for (int r = 0; r < RGW; ++r) {
         const int row = (rgw0 + r) * kRowsPerGroup + i;
         if (row >= p.N)
             continue;
 #pragma unroll
-        for (int tb = 0; tb < BMB; ++tb)
+        for (int tb = 0; tb < WB; ++tb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 16 * tb + 4 * g + v;
+                const int t = 16 * (wtb0 + tb) + 4 * g + v;
                 if (t < ntok)
                     p.Y[(size_t)(tok0 + t) * p.N + row] = f32_to_bf16_bits(p.gscale * acc[r][tb][v]);
             }
@@ -1234,6 +1237,7 @@ typedef void (*GemmKernel)(GemmParams);
 
 struct GemmGeometry {
     int rgw, gw, bmb;      // row groups per wave, waves per workgroup, 16-token blocks per token tile
+    int ts;                // waves sharing one row group's token tile (token split)
     int grid_x, grid_y;    // row tiles, token tiles
 };
 
@@ -1248,6 +1252,13 @@ struct GemmGeometry {
 // threshold it puts two workgroups on some compute unit, as long a critical
 // path at a lower rate per row (fused QKV, n = 320 .. 512: 90 .. 97 us against
 // 74 .. 82 us for 256 rows), below it the 64-row tile was as fast or faster.
+// The 64-row tile with a single 128-token tile runs 8 waves, two per row group,
+// each on 64 of the tokens: twice the waves of the 4-wave form where the grid
+// has one token tile (n = 96 .. 128 on the fused QKV: 36 us against 41 us).
+// With more token tiles its registers (one such workgroup per compute unit)
+// cost more than the waves gain, and with 32- or 64-token tiles it gains
+// nothing.  Each output's sum over K runs in one wave in the same order
+// whatever the tile, so every choice gives the same bits.
 void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
 {
     geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
@@ -1257,17 +1268,19 @@ void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
     const long long tiles256 = (RG + 15) / 16;
     const bool wide = tiles256 * geo->grid_y * 2 >= cus;
     geo->rgw = wide ? 2 : 1;
-    geo->gw = wide ? 8 : 4;
-    geo->grid_x = (int)((RG + geo->rgw * geo->gw - 1) / (geo->rgw * geo->gw));
+    geo->ts = !wide && geo->bmb == 8 && geo->grid_y == 1 ? 2 : 1;
+    geo->gw = wide || geo->ts == 2 ? 8 : 4;
+    const int rows_rg = geo->rgw * geo->gw / geo->ts;   // row groups per workgroup
+    geo->grid_x = (int)((RG + rows_rg - 1) / rows_rg);
 }
 
 template <int RGW, int GW>
 GemmKernel pick_gemm_bmb(int bmb)
 {
     switch (bmb) {
-    case 2: return nvfp4_gemm_kernel<RGW, 2, GW>;
-    case 4: return nvfp4_gemm_kernel<RGW, 4, GW>;
-    default: return nvfp4_gemm_kernel<RGW, 8, GW>;
+    case 2: return nvfp4_gemm_kernel<RGW, 2, GW, 1>;
+    case 4: return nvfp4_gemm_kernel<RGW, 4, GW, 1>;
+    default: return nvfp4_gemm_kernel<RGW, 8, GW, 1>;
     }
 }
 
@@ -1275,6 +1288,8 @@ GemmKernel pick_gemm(const GemmGeometry &geo)
 {
     if (geo.rgw == 2)
         return pick_gemm_bmb<2, 8>(geo.bmb);
+    if (geo.ts == 2)
+        return nvfp4_gemm_kernel<1, 8, 8, 2>;
     return pick_gemm_bmb<1, 4>(geo.bmb);
 }
 
@@ -1596,7 +1611,7 @@ int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup, int *token
         return NVFP4_ERR_SHAPE;
     GemmGeometry geo;
     gemm_geometry_for(n, N, 256, &geo);   // MI355X; the launch itself uses the queried count
-    *rows_per_workgroup = geo.rgw * geo.gw * kRowsPerGroup;
+    *rows_per_workgroup = geo.rgw * geo.gw / geo.ts * kRowsPerGroup;
     *tokens_per_workgroup = geo.bmb * 16;
     *grid_x = geo.grid_x;
     *grid_y = geo.grid_y;
