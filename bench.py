@@ -396,6 +396,14 @@ def cpu_baseline(N, K, n, seconds):
         O.gemv(codes, scales, g, X, nthreads=1)
         t1s.append(time.perf_counter() - t0)
     t1 = float(np.median(t1s[1:]))
+    # One token on all threads: a warm-up and the median of 5.
+    X1 = inputs.activations_bf16(1, K, inputs.act_seed(1, 1))
+    tn1 = []
+    for _ in range(6):
+        t0 = time.perf_counter()
+        O.gemv(codes, scales, g, X1)
+        tn1.append(time.perf_counter() - t0)
+    tn1 = float(np.median(tn1[1:]))
     wb = metrics.weight_bytes(N, K)
     cpu_model = None
     try:
@@ -413,6 +421,8 @@ def cpu_baseline(N, K, n, seconds):
                   % (N, K, n, len(times), t),
         "single_thread": {"value": round(wb / t1 / 1e9, 4), "gemv_tokens_per_s": round(n / t1, 2),
                           "sample": "same call, median of 3 after a warm-up, %.3f s per call" % t1},
+        "n1": {"value": round(wb / tn1 / 1e9, 4), "gemv_tokens_per_s": round(1 / tn1, 2),
+               "sample": "one token, all threads, median of 5 after a warm-up, %.4f s per call" % tn1},
         "host": {"cpu_model": cpu_model, "os_cpu_count": os.cpu_count()},
     }
 
