@@ -218,8 +218,10 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
 /* Tile shape and grid nvfp4_gemm uses for (n, N, K) on MI355X: weight rows
  * and tokens per workgroup, workgroups along rows and along tokens.  Tokens:
  * the smallest of 32 / 64 / 128 holding n.  Rows: 256 (8 waves) when that grid
- * gives at least half of the 256 compute units a workgroup, else 64 (4 waves,
- * or 8 waves sharing the row groups' tokens when there is one 128-token tile).
+ * gives at least half of the 256 compute units a workgroup (also with 64-token
+ * tiles instead of two or more 128-token tiles where only they get there),
+ * else 64 (4 waves, or 8 waves sharing the row groups' tokens when there is
+ * one 128-token tile).
  * Pure host function; returns a status. */
 int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup,
                         int *tokens_per_workgroup, int *grid_x, int *grid_y);

@@ -1252,6 +1252,12 @@ struct GemmGeometry {
 // threshold it puts two workgroups on some compute unit, as long a critical
 // path at a lower rate per row (fused QKV, n = 320 .. 512: 90 .. 97 us against
 // 74 .. 82 us for 256 rows), below it the 64-row tile was as fast or faster.
+// Where two or more 128-token tiles leave the grid under that threshold but
+// 64-token tiles reach it, 64-token tiles with the 256-row tile are taken:
+// twice the weight reads, but the faster tile (fused QKV, n = 160 .. 256:
+// 50 .. 54 us against 61 .. 63 us).  With one 128-token tile the token-split
+// 64-row tile below is faster (n = 96 .. 128: 38.7 / 38.8 us against 38.9 /
+// 39.7 us with 64-token tiles).
 // The 64-row tile with a single 128-token tile runs 8 waves, two per row group,
 // each on 64 of the tokens: twice the waves of the 4-wave form where the grid
 // has one token tile (n = 96 .. 128 on the fused QKV: 36 us against 41 us).
@@ -1262,11 +1268,18 @@ struct GemmGeometry {
 void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
 {
     geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
-    const int bm = 16 * geo->bmb;
     const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    geo->grid_y = (n + bm - 1) / bm;
+    geo->grid_y = (n + 16 * geo->bmb - 1) / (16 * geo->bmb);
     const long long tiles256 = (RG + 15) / 16;
-    const bool wide = tiles256 * geo->grid_y * 2 >= cus;
+    bool wide = tiles256 * geo->grid_y * 2 >= cus;
+    if (!wide && geo->bmb == 8 && geo->grid_y >= 2) {
+        const int gy64 = (n + 63) / 64;
+        if (tiles256 * gy64 * 2 >= cus) {   // 64-token tiles make the grid wide enough
+            geo->bmb = 4;
+            geo->grid_y = gy64;
+            wide = true;
+        }
+    }
     geo->rgw = wide ? 2 : 1;
     geo->ts = !wide && geo->bmb == 8 && geo->grid_y == 1 ? 2 : 1;
     geo->gw = wide || geo->ts == 2 ? 8 : 4;

@@ -188,12 +188,12 @@ def test_gemm_guard_band_untouched(n):
 
 def test_gemm_identity_across_row_tiles_full_size():
     """Fused QKV weight: n = 40 (64 rows x 64 tokens), 100 (64 x 128, one token
-    tile: 8 waves, two per row group), 200 (64 x 128, 4 waves) and 1024
-    (256 x 128, 8 waves) give the same bits for the tokens they share."""
+    tile: 8 waves, two per row group), 200 (256 x 64) and 1024 (256 x 128)
+    give the same bits for the tokens they share."""
     N, K = 14336, 5120
     shapes = [nv.gemm_geometry(n, N, K)[:2] for n in (40, 100, 200, 1024)]
     say("gemm tiles", shapes)
-    assert shapes == [(64, 64), (64, 128), (64, 128), (256, 128)]
+    assert shapes == [(64, 64), (64, 128), (256, 64), (256, 128)]
     W = inputs.weights_f32(N, K, inputs.weight_seed(1))
     codes, scales, g = O.quantize(W)
     pw = packed(codes, scales, g, N, K)

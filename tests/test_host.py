@@ -187,8 +187,12 @@ def test_gemm_geometry_rule():
     # row tile: 256 rows (8 waves) once its grid gives at least half of the
     # 256 compute units a workgroup, else 64 rows (4 waves, two per unit).
     # Fused QKV, 896 row groups = 56 tiles of 256 rows:
-    assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)     # 56 workgroups: under half
-    assert nv.gemm_geometry(256, 14336, 5120) == (64, 128, 224, 2)     # 112: under half
+    assert nv.gemm_geometry(100, 14336, 5120) == (64, 128, 224, 1)     # 56 workgroups: under half
+    # 2 tiles of 128 tokens give 112 (under half), 4 of 64 tokens 224: 64-token tiles, 256 rows
+    assert nv.gemm_geometry(256, 14336, 5120) == (256, 64, 56, 4)
+    assert nv.gemm_geometry(160, 14336, 5120) == (256, 64, 56, 3)
+    # one 128-token tile (56) and 2 of 64 tokens (112) are both under half: 64 rows x 128 tokens
+    assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)
     assert nv.gemm_geometry(320, 14336, 5120) == (256, 128, 56, 3)     # 168
     assert nv.gemm_geometry(512, 14336, 5120) == (256, 128, 56, 4)     # 224
     assert nv.gemm_geometry(1024, 14336, 5120) == (256, 128, 56, 8)    # 448
@@ -197,7 +201,11 @@ def test_gemm_geometry_rule():
     assert nv.gemm_geometry(128, 16384, 5120) == (64, 128, 256, 1)
     # 5120 rows (20 tiles of 256 rows): 7 token tiles give 140 workgroups, 6 give 120
     assert nv.gemm_geometry(896, 5120, 6144) == (256, 128, 20, 7)
-    assert nv.gemm_geometry(768, 5120, 6144) == (64, 128, 80, 6)
+    assert nv.gemm_geometry(768, 5120, 6144) == (256, 64, 20, 12)      # 6 x 128 tokens: 120; 12 x 64: 240
+    assert nv.gemm_geometry(300, 5120, 6144) == (64, 128, 80, 3)       # neither reaches half
+    # 16384 rows, one 128-token tile: 64 workgroups of 256 rows; 64-token tiles would reach half,
+    # but with a single 128-token tile the 64-row token-split tile is kept
+    assert nv.gemm_geometry(128, 16384, 5120) == (64, 128, 256, 1)
     # 34816 rows (136 tiles): the 256-row tile is wide enough at one token tile
     assert nv.gemm_geometry(40, 34816, 5120) == (256, 64, 136, 1)
     for n, N in ((17, 1), (300, 37), (5000, 100), (1 << 20, 16)):
