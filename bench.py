@@ -67,7 +67,7 @@ EXTRA_SHAPES = [
 ]
 EXTRA_N = [1, 2, 4, 8, 16]
 # Prefill (many-token) GEMM sweep on the fused QKV weight.
-PREFILL_N = [32, 64, 128, 256, 512, 1024, 2048]
+PREFILL_N = [32, 64, 128, 256, 384, 512, 768, 1024, 2048]
 ROTATION_BYTES = 1 << 30
 # The pages' own numbers, on another GPU and memory system (GB10, sm_121):
 # context for the reader, never a target and never the vs_baseline figure.

@@ -1243,7 +1243,7 @@ struct GemmGeometry {
 
 // Tile shape of the prefill GEMM for n tokens of an N x K weight on `cus`
 // compute units.  The token tile is the smallest of 32 / 64 / 128 tokens that
-// holds n (capped at 128).  The row tile is 256 rows (8 waves x 2 row groups,
+// holds n (capped at 128; for n > 128 see the 256-row choice below).  The row tile is 256 rows (8 waves x 2 row groups,
 // one workgroup per compute unit), which shares each X tile among the most
 // rows and measured the fastest per row, once its grid gives at least half
 // the compute units a workgroup; below that, 64 rows (4 waves x 1 row group,
@@ -1252,10 +1252,12 @@ struct GemmGeometry {
 // threshold it puts two workgroups on some compute unit, as long a critical
 // path at a lower rate per row (fused QKV, n = 320 .. 512: 90 .. 97 us against
 // 74 .. 82 us for 256 rows), below it the 64-row tile was as fast or faster.
-// Where two or more 128-token tiles leave the grid under that threshold but
-// 64-token tiles reach it, 64-token tiles with the 256-row tile are taken:
-// twice the weight reads, but the faster tile (fused QKV, n = 160 .. 256:
-// 50 .. 54 us against 61 .. 63 us).  With one 128-token tile the token-split
+// Beyond one 128-token tile (n > 128) the 256-row tile may also take 96- or
+// 64-token tiles: more weight reads and a lower rate per token, but more
+// workgroups in as few rounds.  Fused QKV: 96-token tiles at n = 288 .. 384
+// take 65 .. 68 us against 75 .. 76 us, at n = 640 / 768 132 / 138 against
+// 145 / 148 us; 64-token tiles at n = 160 .. 256 50 .. 54 us against 61 .. 63
+// us for the 64-row tile.  With one 128-token tile (n <= 128) the token-split
 // 64-row tile below is faster (n = 96 .. 128: 38.7 / 38.8 us against 38.9 /
 // 39.7 us with 64-token tiles).
 // The 64-row tile with a single 128-token tile runs 8 waves, two per row group,
@@ -1272,12 +1274,24 @@ void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
     geo->grid_y = (n + 16 * geo->bmb - 1) / (16 * geo->bmb);
     const long long tiles256 = (RG + 15) / 16;
     bool wide = tiles256 * geo->grid_y * 2 >= cus;
-    if (!wide && geo->bmb == 8 && geo->grid_y >= 2) {
-        const int gy64 = (n + 63) / 64;
-        if (tiles256 * gy64 * 2 >= cus) {   // 64-token tiles make the grid wide enough
-            geo->bmb = 4;
-            geo->grid_y = gy64;
-            wide = true;
+    if (n > 128) {
+        // Among the token tiles whose 256-row grid reaches half the compute
+        // units, the least (rounds x tokens per tile / measured rate per token
+        // of that tile: 1.0, 0.84, 0.70 for 128, 96, 64), 128 first on ties.
+        static const int bms[3] = {8, 6, 4}, rate[3] = {100, 84, 70};
+        long long best = -1;
+        for (int j = 0; j < 3; ++j) {
+            const long long gy = (n + 16 * bms[j] - 1) / (16 * bms[j]);
+            const long long wgs = tiles256 * gy;
+            if (wgs * 2 < cus)
+                continue;
+            const long long cost = (wgs + cus - 1) / cus * 16 * bms[j] * 10000 / rate[j];
+            if (best < 0 || cost < best) {
+                best = cost;
+                geo->bmb = bms[j];
+                geo->grid_y = (int)gy;
+                wide = true;
+            }
         }
     }
     geo->rgw = wide ? 2 : 1;
@@ -1293,6 +1307,10 @@ GemmKernel pick_gemm_bmb(int bmb)
     switch (bmb) {
     case 2: return nvfp4_gemm_kernel<RGW, 2, GW, 1>;
     case 4: return nvfp4_gemm_kernel<RGW, 4, GW, 1>;
+    case 6:
+        if constexpr (GW == 8)
+            return nvfp4_gemm_kernel<RGW, 6, GW, 1>;   // 96-token tiles: 256-row tile only
+        return nullptr;
     default: return nvfp4_gemm_kernel<RGW, 8, GW, 1>;
     }
 }
@@ -1607,7 +1625,10 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uin
     p.K = K;
     p.T = (K + kTileK - 1) / kTileK;
     p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
-    hipLaunchKernelGGL(pick_gemm(geo), dim3(geo.grid_x, geo.grid_y),
+    GemmKernel kern = pick_gemm(geo);
+    if (!kern)
+        return NVFP4_ERR_SHAPE;
+    hipLaunchKernelGGL(kern, dim3(geo.grid_x, geo.grid_y),
                        dim3(geo.gw * 64), 0,
                        (hipStream_t)stream, p);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;

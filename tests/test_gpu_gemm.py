@@ -124,7 +124,7 @@ def test_gemm_agrees_with_gemv_on_decode_batch():
     assert_parity(y_bits(nv.gemv(pw, x_to_dev(X))), Yref, Aref, "gemv")
 
 
-@pytest.mark.parametrize("n", [256, 1000])
+@pytest.mark.parametrize("n", [256, 320, 1000])
 def test_gemm_full_size_sampled(n):
     """Fused QKV 14336 x 5120 at prefill sizes, launched as the bench times
     it; 1500 outputs sampled and computed one by one by the oracle."""
@@ -188,16 +188,16 @@ def test_gemm_guard_band_untouched(n):
 
 def test_gemm_identity_across_row_tiles_full_size():
     """Fused QKV weight: n = 40 (64 rows x 64 tokens), 100 (64 x 128, one token
-    tile: 8 waves, two per row group), 200 (256 x 64) and 1024 (256 x 128)
-    give the same bits for the tokens they share."""
+    tile: 8 waves, two per row group), 200 (256 x 64), 320 (256 x 96) and
+    1024 (256 x 128) give the same bits for the tokens they share."""
     N, K = 14336, 5120
-    shapes = [nv.gemm_geometry(n, N, K)[:2] for n in (40, 100, 200, 1024)]
+    shapes = [nv.gemm_geometry(n, N, K)[:2] for n in (40, 100, 200, 320, 1024)]
     say("gemm tiles", shapes)
-    assert shapes == [(64, 64), (64, 128), (256, 64), (256, 128)]
+    assert shapes == [(64, 64), (64, 128), (256, 64), (256, 96), (256, 128)]
     W = inputs.weights_f32(N, K, inputs.weight_seed(1))
     codes, scales, g = O.quantize(W)
     pw = packed(codes, scales, g, N, K)
     X = x_to_dev(inputs.activations_bf16(1024, K, 81))
     big = y_bits(nv.gemm(pw, X))
-    for n in (40, 100, 200):
+    for n in (40, 100, 200, 320):
         assert np.array_equal(y_bits(nv.gemm(pw, X[:n].contiguous())), big[:n]), n

@@ -193,14 +193,16 @@ def test_gemm_geometry_rule():
     assert nv.gemm_geometry(160, 14336, 5120) == (256, 64, 56, 3)
     # one 128-token tile (56) and 2 of 64 tokens (112) are both under half: 64 rows x 128 tokens
     assert nv.gemm_geometry(128, 14336, 5120) == (64, 128, 224, 1)
-    assert nv.gemm_geometry(320, 14336, 5120) == (256, 128, 56, 3)     # 168
+    assert nv.gemm_geometry(320, 14336, 5120) == (256, 96, 56, 4)      # 96-token tiles: 224 in one round
     assert nv.gemm_geometry(512, 14336, 5120) == (256, 128, 56, 4)     # 224
     assert nv.gemm_geometry(1024, 14336, 5120) == (256, 128, 56, 8)    # 448
-    # 16384 rows, 2 token tiles: 128 workgroups of 256 rows is exactly half
-    assert nv.gemm_geometry(256, 16384, 5120) == (256, 128, 64, 2)
+    # 16384 rows: 128-token tiles give 128 workgroups (half), 64-token tiles 256 in one round
+    assert nv.gemm_geometry(256, 16384, 5120) == (256, 64, 64, 4)
+    assert nv.gemm_geometry(640, 14336, 5120) == (256, 96, 56, 7)      # 392 in two rounds of 96 tokens
+    assert nv.gemm_geometry(2048, 14336, 5120) == (256, 128, 56, 16)
     assert nv.gemm_geometry(128, 16384, 5120) == (64, 128, 256, 1)
     # 5120 rows (20 tiles of 256 rows): 7 token tiles give 140 workgroups, 6 give 120
-    assert nv.gemm_geometry(896, 5120, 6144) == (256, 128, 20, 7)
+    assert nv.gemm_geometry(896, 5120, 6144) == (256, 96, 20, 10)
     assert nv.gemm_geometry(768, 5120, 6144) == (256, 64, 20, 12)      # 6 x 128 tokens: 120; 12 x 64: 240
     assert nv.gemm_geometry(300, 5120, 6144) == (64, 128, 80, 3)       # neither reaches half
     # 16384 rows, one 128-token tile: 64 workgroups of 256 rows; 64-token tiles would reach half,
