@@ -581,7 +581,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 weights (e2m1 + e4m3 block scale), bf16 activations, fp32 accumulate",
+        "dtype": "bf16",
+        "arithmetic": "bf16 MFMA operands (NVFP4 weights decoded exactly: e2m1 codes to bf16, e4m3 block "
+                      "scale applied with fp32 FMAs), fp32 accumulation, bf16 output",
         "data": "synthetic: W ~ N(0,0.02) fp32 quantised on the GPU, x ~ N(0,1) bf16; %d distinct weight copies rotated (%.2f GiB, cold against the 256 MB Infinity Cache)" % (rot.count, rot.count * wb / 2**30),
         "config": {"workload": args.workload, "N": N, "K": K, "n_tokens": n,
                    "qkv_rows": list(QKV_ROWS) if qkv else None,
