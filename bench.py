@@ -571,7 +571,9 @@ def main():
     value = wb / t_call / 1e9
     wg, waves, tpw = nv.launch_geometry(n, N, K)
     result = {
-        "metric": "effective weight GB/s (NVFP4 weight bytes N*K*9/16 per call / time per call)",
+        "metric": "effective weight GB/s (% of HBM peak) and GEMV-tokens/s vs n=1..16",
+        "value_is": "effective weight GB/s at the headline n: NVFP4 weight bytes N*K*9/16 per call / time per call "
+                    "(frac_hbm_peak, gemv_tokens_per_s and the per-n sweep carry the rest of the metric)",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
