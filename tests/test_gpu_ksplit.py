@@ -200,3 +200,25 @@ def test_ksplit_graph_replays_equal_eager(ffn_down):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y_bits(Y), eager), r
+
+
+def test_ksplit_full_decode_shape_explicit_parts():
+    """ssm_qkvz 16384 x 5120 (one pass, so the library takes one part) cut
+    into 2 parts on request: parity at n = 16 against the oracle."""
+    say("qkvz 16384x5120 in 2 K parts")
+    N, K = 16384, 5120
+    pw, codes, scales, g = case(N, K, inputs.weight_seed(3))
+    assert nv.gemv_kparts(N, K) == 1
+    X = inputs.activations_bf16(16, K, inputs.act_seed(3, 16), row_scale=True)
+    Y = y_bits(nv.gemv_ws(pw, x_to_dev(X), 2))
+    Yref, Aref = O.gemv(codes, scales, g, X)
+    assert_parity(Y, Yref, Aref, "qkvz 16384x5120 n=16, 2 K parts")
+
+
+def test_ksplit_identity_every_n():
+    say("k parts identity for every n")
+    pw, _, _, _ = case(333, 12304, 9444)
+    X = x_to_dev(inputs.activations_bf16(16, 12304, 9445))
+    full = y_bits(nv.gemv_ws(pw, X, 5))
+    for n in range(1, 16):
+        assert np.array_equal(y_bits(nv.gemv_ws(pw, X[:n].contiguous(), 5)), full[:n]), n
