@@ -65,8 +65,15 @@ typedef enum {
  * up to 16 concurrent sequences, Atlas PR #266 A/B table, C = 1..16). */
 #define NVFP4_MAX_TOKENS 16
 
-/* Byte sizes of the packed device layout for an N x K weight.  0 if N <= 0
- * or K <= 0 or K % 16 != 0. */
+/* Byte sizes of the packed device layout for an N x K weight: the weight in
+ * the order the GEMV kernels load it, built once at load time.  The pages
+ * trace their fast path to exactly this: the wide kernel ran fast only on a
+ * weight copy laid out for it, and the fix they propose is to emit that copy
+ * when the weight is (re)quantised (Atlas PR #266 automated review page,
+ * "Tiebreaker" comment and the "Complete picture" follow-up).  Rows are padded
+ * to 16 and K to 128, so the sizes are ceil(N/16)*16 * ceil(K/128)*128 / 2
+ * bytes of codes and a sixteenth of that count of scale bytes, computed in
+ * 64-bit arithmetic.  0 if N <= 0 or K <= 0 or K % 16 != 0. */
 size_t nvfp4_packed_codes_bytes(int N, int K);
 size_t nvfp4_packed_scales_bytes(int N, int K);
 
@@ -100,13 +107,21 @@ int nvfp4_quantize_packed(const void *W, int dtype, int N, int K, uint8_t *codes
                           uint8_t *scales_packed, float *tensor_scale, void *stream);
 
 /* Reorder canonical codes/scales (device) into the packed device layout
- * (device buffers of nvfp4_packed_*_bytes; the padding is written as zeros).
- * One-time, at weight load.  Errors: NULL, RANGE, SHAPE, ALIGN (packed
- * buffers must be 16-byte aligned), LAUNCH. */
+ * (device buffers of nvfp4_packed_*_bytes; the padding is written as zeros):
+ * the one-time layout step the pages ask for, the weight copy the fast kernel
+ * reads, made once at load instead of on every call (Atlas PR #266 automated
+ * review page, "Tiebreaker" comment: the wide GEMM's fast path needs such a
+ * copy, and emitting it at load is named as the fix).  A pure byte gather
+ * (nibble order unchanged), so packing loses nothing.  Errors: NULL, RANGE,
+ * SHAPE, ALIGN (packed buffers must be 16-byte aligned), LAUNCH, DEVICE. */
 int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K,
                uint8_t *codes_packed, uint8_t *scales_packed, void *stream);
 
-/* Y[n][N] = X[n][K] . dequant(W)^T for 1 <= n <= 16 tokens.
+/* Y[n][N] = X[n][K] . dequant(W)^T for 1 <= n <= 16 tokens: one projection
+ * of n concurrent decode tokens that reads the weight once for all of them
+ * (Atlas PR #266 conversation page, PR description "What it does": a tile of
+ * tokens shares one read of the projection weight instead of one read per
+ * token).  Here the tile is the whole batch of up to 16 tokens.
  * Wq / Wscale: packed layout (nvfp4_pack), 16-byte aligned.
  * X: bf16 [n][K], 16-byte aligned.  Y: bf16 [n][N], 2-byte aligned.
  * Each token's result is bit-identical to the same token computed alone
@@ -196,6 +211,20 @@ int nvfp4_schedule_greedy(int n, int width, uint8_t *widths, int max_tiles);
 int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves,
                           int *tiles_per_wave);
 
+/* The GEMV kernel a call launches for (n, N, K) with ks K parts (ks = 1:
+ * nvfp4_gemv, nvfp4_gemv_qkv and every tile of nvfp4_gemv_sched; ks = 0: the
+ * part count nvfp4_gemv_ws takes, nvfp4_gemv_kparts(N, K); ks > 1: that many
+ * parts of nvfp4_gemv_ws).  The kernel is specialised on five values, which
+ * variant (HOST int[5]) receives: [0] 128-column tiles of each wave's K-slice
+ * in one pass (1 .. 8), [1] groups of four tokens carried, ceil(n/4), [2] 1 if
+ * every wave owns exactly [0] tiles of every pass (no column predication),
+ * [3] K-chunk passes inside the launch (1 = one pass), [4] K parts.  Lets a
+ * caller, and the tests, know which specialisation serves a shape (the tile
+ * schedule and its variants are the dispatch the PR description describes,
+ * here picked from the shape).  Pure host function; returns a status (RANGE,
+ * SHAPE as nvfp4_gemv_ws would). */
+int nvfp4_gemv_variant(int n, int N, int K, int ks, int *variant);
+
 /* Largest token count of one nvfp4_gemm call. */
 #define NVFP4_MAX_GEMM_TOKENS (1 << 20)
 
@@ -225,40 +254,6 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
  * Pure host function; returns a status. */
 int nvfp4_gemm_geometry(int n, int N, int K, int *rows_per_workgroup,
                         int *tokens_per_workgroup, int *grid_x, int *grid_y);
-
-/* Paths of nvfp4_block_rate. */
-#define NVFP4_RATE_MFMA 0
-#define NVFP4_RATE_VALU 1
-
-/* Measurement aid, not part of the GEMV path: the issue rate of the
- * arithmetic for one 16-element block of a 16-row group times n tokens, on
- * register data (no memory traffic), for the two ways to do it on gfx950.
- * NVFP4_RATE_MFMA is nvfp4_gemv's sequence (two fp4->bf16 converts, one
- * 16x16x16 bf16 MFMA with the tokens as M, ceil(n/4) scale FMAs);
- * NVFP4_RATE_VALU the best VALU form found (the same converts, then per token
- * an LDS read of its 4 activations, two v_dot2_f32_bf16 and one scale FMA).
- * This is the measurement behind choosing MFMA for n = 1..16 (the pages'
- * kernels are VALU/tensor-core designs for another GPU).  Runs 256 workgroups
- * of 8 waves (two per SIMD), each wave `blocks` blocks (rounded down to a
- * multiple of 8, with independent codes per block as loaded tiles have); the
- * time of the launch divided by that count is the time of one block on every
- * SIMD of the chip, two waves at once.  n in {1, 2, 4, 8, 12, 16}.  sink:
- * DEVICE, at least 256*512*4 bytes, 4-byte aligned, receives meaningless
- * values.  Errors: NULL, RANGE (path, n, blocks < 8, sink_bytes), ALIGN,
- * LAUNCH. */
-int nvfp4_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes,
-                     void *stream);
-
-/* Measurement aid, not part of the GEMV path: reads `bytes` bytes of `buf`
- * (DEVICE, 16-byte aligned, bytes a positive multiple of 16) once with the
- * streaming pattern that reads fastest on MI355X (1024-thread workgroups,
- * contiguous chunks, four 16-byte non-temporal loads in flight per lane) and
- * writes a checksum of the data to *sink (DEVICE, 4 bytes) so that no load
- * is dead.  Timing it gives the achievable HBM read ceiling the GEMV's
- * effective weight bandwidth is compared with (the pages compare their
- * kernels with a STREAM-measured ceiling in the same way).  Asynchronous on
- * `stream`; errors: NULL, RANGE (bytes), ALIGN, DEVICE, LAUNCH. */
-int nvfp4_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);

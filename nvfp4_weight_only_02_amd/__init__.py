@@ -80,24 +80,22 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_launch_geometry.restype = _i32
         L.nvfp4_launch_geometry.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32),
                                             ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        L.nvfp4_gemv_variant.restype = _i32
+        L.nvfp4_gemv_variant.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]
         L.nvfp4_gemm.restype = _i32
         L.nvfp4_gemm.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _vp]
         L.nvfp4_gemm_geometry.restype = _i32
         L.nvfp4_gemm_geometry.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
-        L.nvfp4_read_stream.restype = _i32
-        L.nvfp4_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-        L.nvfp4_block_rate.restype = _i32
-        L.nvfp4_block_rate.argtypes = [_i32, _i32, _i32, _vp, ctypes.c_size_t, _vp]
         L.nvfp4_strerror.restype = ctypes.c_char_p
         L.nvfp4_strerror.argtypes = [_i32]
         _lib = L
     return _lib
 
 
-def header_functions() -> list:
-    """Names of the functions include/nvfp4.h declares."""
-    text = open(HEADER_PATH).read()
+def header_functions(path: str = HEADER_PATH) -> list:
+    """Names of the functions a header under include/ declares (nvfp4.h by default)."""
+    text = open(path).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", text, re.M)))
 
 
@@ -156,6 +154,15 @@ def launch_geometry(n: int, N: int, K: int):
     _check(lib().nvfp4_launch_geometry(n, N, K, ctypes.byref(wg), ctypes.byref(wv),
                                        ctypes.byref(tpw)), "nvfp4_launch_geometry")
     return wg.value, wv.value, tpw.value
+
+
+def gemv_variant(n: int, N: int, K: int, ks: int = 1) -> tuple:
+    """(tiles per wave, token groups of four, exact, K-chunk passes, K parts)
+    of the GEMV kernel a call launches; ks = 1 for nvfp4_gemv, 0 for
+    nvfp4_gemv_ws's own part count, > 1 for that many parts."""
+    v = (_i32 * 5)()
+    _check(lib().nvfp4_gemv_variant(n, N, K, ks, v), "nvfp4_gemv_variant")
+    return tuple(v)
 
 
 def gemm_geometry(n: int, N: int, K: int):
@@ -300,6 +307,8 @@ def gemv_sched(w: PackedWeight, X: torch.Tensor, tile_widths, out: torch.Tensor 
     n = X.shape[0]
     Y = out if out is not None else torch.empty((n, w.N), dtype=torch.bfloat16, device=X.device)
     _dev(Y, torch.bfloat16, "out")
+    if Y.shape != (n, w.N):
+        raise ValueError("out must be [n, N]")
     widths = (ctypes.c_uint8 * max(len(tile_widths), 1))(*[int(v) for v in tile_widths])
     _check(lib().nvfp4_gemv_sched(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                                   Y.data_ptr(), n, w.N, w.K, widths, len(tile_widths),
@@ -319,25 +328,6 @@ def gemm(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None
     _check(lib().nvfp4_gemm(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                             Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemm")
     return Y
-
-
-RATE_MFMA, RATE_VALU = 0, 1
-
-
-def block_rate(path: int, n: int, blocks: int, sink: torch.Tensor, stream=None) -> None:
-    """Launch the per-block arithmetic-rate probe (RATE_MFMA or RATE_VALU)
-    for n tokens; ``sink`` is a float32 device tensor of >= 256*512 elements."""
-    _dev(sink, torch.float32, "sink")
-    _check(lib().nvfp4_block_rate(int(path), int(n), int(blocks), sink.data_ptr(), sink.numel() * 4,
-                                  _stream(stream)), "nvfp4_block_rate")
-
-
-def read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """Read every byte of ``buf`` once (measurement aid for the read ceiling)."""
-    _dev(buf, torch.uint8, "buf")
-    _dev(sink, torch.int32, "sink")
-    _check(lib().nvfp4_read_stream(buf.data_ptr(), buf.numel(), sink.data_ptr(), _stream(stream)),
-           "nvfp4_read_stream")
 
 
 def gemv_qkv(w: PackedWeight, X: torch.Tensor, rows, out_off, ldy: int,

@@ -1,8 +1,9 @@
-"""Build libnvfp4.so (gfx950) in-tree with hipcc.
+"""Build the HIP libraries (gfx950) in-tree with hipcc.
 
-``python -m nvfp4_weight_only_02_amd.build`` compiles every HIP source of the
-library.  The flags keep hipcc from emitting packed-fp32 VALU instructions
-(``-packed-fp32-ops``) for every kernel.
+``python -m nvfp4_weight_only_02_amd.build`` compiles libnvfp4.so (the decode
+projection, C ABI in include/nvfp4.h) and libnvfp4_probes.so (measurement
+aids beside it, include/nvfp4_probes.h).  The flags keep hipcc from emitting
+packed-fp32 VALU instructions (``-packed-fp32-ops``) for every kernel.
 """
 from __future__ import annotations
 
@@ -14,8 +15,11 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "nvfp4.hip"), os.path.join(PKG, "csrc", "block_rate.hip")]
 LIB = os.path.join(PKG, "libnvfp4.so")
+PROBES_LIB = os.path.join(PKG, "libnvfp4_probes.so")
+# (library, its sources)
+TARGETS = [(LIB, [os.path.join(PKG, "csrc", "nvfp4.hip")]),
+           (PROBES_LIB, [os.path.join(PKG, "csrc", "probes.hip")])]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -60,10 +64,10 @@ def check_resources(remarks: str) -> None:
         raise RuntimeError("GEMV/GEMM kernels must not spill or use scratch:\n  " + "\n  ".join(bad))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always) and return its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-Rpass-analysis=kernel-resource-usage"] + SOURCES + ["-o", tmp]
+def build_one(lib: str, sources: list, verbose: bool = False) -> str:
+    """Compile one library (always) and return its path."""
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-Rpass-analysis=kernel-resource-usage"] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -90,7 +94,14 @@ def build(verbose: bool = False) -> str:
         raise
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every library (always); returns the path of libnvfp4.so."""
+    for lib, sources in TARGETS:
+        build_one(lib, sources, verbose)
     return LIB
 
 

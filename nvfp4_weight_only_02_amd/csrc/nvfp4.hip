@@ -71,6 +71,17 @@ constexpr int kSlots = 8;                        // row-group partials parked in
 constexpr int kMaxK = 1 << 18;                   // keeps every buffer offset within 32 bits
 constexpr int kMaxKParts = 64;                   // K parts of a split launch
 
+// 16-row groups of N rows and 128-column tiles of K columns, rounded up in
+// 64-bit arithmetic (no int near INT_MAX overflows).
+constexpr long long row_groups(long long N)
+{
+    return (N + kRowsPerGroup - 1) / kRowsPerGroup;
+}
+constexpr long long k_tiles(long long K)
+{
+    return (K + kTileK - 1) / kTileK;
+}
+
 struct GemvParams {
     const u32x4 *codes;    // packed codes, [RG][T][64 lanes] x 16 B
     const u32x2 *scales;   // packed scales, [RG][T][16 rows] x 8 B
@@ -996,36 +1007,6 @@ __global__ void nvfp4_gscale_kernel(float *ts)
     ts[0] = (float)((double)ts[1] / 2688.0);
 }
 
-// ---- read-stream ceiling (measurement aid) ------------------------------------
-
-constexpr int kReadThreads = 1024;
-constexpr int kReadUnroll = 4;
-
-// Workgroup w reads its contiguous chunk of `chunk16` 16-byte words, four
-// non-temporal loads in flight per lane; the xor of everything read goes to
-// *sink only if it equals a value no real data produces here, so the loads
-// stay live and nothing is written in practice.
-__global__ __launch_bounds__(kReadThreads) void nvfp4_read_stream_kernel(const u32x4 *buf, size_t n16,
-                                                                         size_t chunk16, unsigned *sink)
-{
-    const size_t s0 = (size_t)blockIdx.x * chunk16;
-    const size_t s1 = s0 + chunk16 < n16 ? s0 + chunk16 : n16;
-    u32 acc = 0;
-    for (size_t o = s0 + threadIdx.x; o < s1; o += (size_t)kReadThreads * kReadUnroll) {
-        u32x4 v[kReadUnroll];
-#pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u) {
-            const size_t q = o + (size_t)u * kReadThreads;
-            v[u] = q < s1 ? __builtin_nontemporal_load(buf + q) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u)
-            acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
-    }
-    if (acc == 0x9E3779B9u)
-        sink[0] = acc;
-}
-
 // ---- host side ---------------------------------------------------------------
 
 typedef void (*GemvKernel)(GemvParams);
@@ -1033,10 +1014,10 @@ typedef void (*GemvKernel)(GemvParams);
 template <int MT, int NV>
 GemvKernel pick_exact(bool exact, bool chunked, bool split)
 {
-    // Several chunks imply more than 64 tiles split into chunks of at most
-    // kMaxTilesChunked tiles per wave: 4 <= MT <= kMaxTilesChunked for every
-    // K up to 262144.  A K part is never chunked.
-    if constexpr (MT >= 4 && MT <= kMaxTilesChunked) {
+    // Several chunks imply more than 64 tiles cut into kc = ceil(T/56)
+    // chunks, so MT = ceil(T/(8*kc)) is 5, 6 or 7 for every K up to 262144
+    // (T = 65 .. 2048).  A K part is never chunked.
+    if constexpr (MT >= 5 && MT <= kMaxTilesChunked) {
         if (chunked && !split)
             return exact ? nvfp4_gemv_kernel<MT, NV, true, true, false>
                          : nvfp4_gemv_kernel<MT, NV, false, true, false>;
@@ -1118,8 +1099,8 @@ int current_device_info(int *cus)
 // row-group range of its part.
 bool geometry_for(int N, int K, int cus, int ks, Geometry *geo)
 {
-    const int T = (K + kTileK - 1) / kTileK;
-    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int T = (int)k_tiles(K);
+    const long long RG = row_groups(N);
     if (ks < 1 || ks > T)
         return false;
     geo->ks = ks;
@@ -1152,8 +1133,8 @@ bool geometry_for(int N, int K, int cus, int ks, Geometry *geo)
 // halve (or better) the X each compute unit loads.
 int ksplit_for(int N, int K)
 {
-    const int T = (K + kTileK - 1) / kTileK;
-    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int T = (int)k_tiles(K);
+    const long long RG = row_groups(N);
     if (T <= kWaves * kMaxTilesPerWave)
         return 1;
     int best = 1;
@@ -1270,7 +1251,7 @@ struct GemmGeometry {
 void gemm_geometry_for(int n, int N, int cus, GemmGeometry *geo)
 {
     geo->bmb = n <= 32 ? 2 : (n <= 64 ? 4 : 8);
-    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const long long RG = row_groups(N);
     geo->grid_y = (n + 16 * geo->bmb - 1) / (16 * geo->bmb);
     const long long tiles256 = (RG + 15) / 16;
     bool wide = tiles256 * geo->grid_y * 2 >= cus;
@@ -1350,8 +1331,8 @@ GemvParams make_params(const uint8_t *Wq, const uint8_t *Wscale, float gscale, c
     p.n = n;
     p.N = N;
     p.K = K;
-    p.T = (K + kTileK - 1) / kTileK;
-    p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    p.T = (int)k_tiles(K);
+    p.RG = (int)row_groups(N);
     p.start1 = N;
     p.start2 = N;
     p.off0 = p.off1 = p.off2 = 0;
@@ -1383,8 +1364,8 @@ size_t nvfp4_packed_codes_bytes(int N, int K)
 {
     if (N <= 0 || K <= 0 || K % 16 != 0)
         return 0;
-    const size_t RG = (size_t)(N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const size_t T = (size_t)(K + kTileK - 1) / kTileK;
+    const size_t RG = (size_t)row_groups(N);
+    const size_t T = (size_t)k_tiles(K);
     return RG * T * 1024;
 }
 
@@ -1392,8 +1373,8 @@ size_t nvfp4_packed_scales_bytes(int N, int K)
 {
     if (N <= 0 || K <= 0 || K % 16 != 0)
         return 0;
-    const size_t RG = (size_t)(N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const size_t T = (size_t)(K + kTileK - 1) / kTileK;
+    const size_t RG = (size_t)row_groups(N);
+    const size_t T = (size_t)k_tiles(K);
     return RG * T * 128;
 }
 
@@ -1448,8 +1429,8 @@ int nvfp4_quantize_packed(const void *W, int dtype, int N, int K, uint8_t *codes
     long long grid = (n + 255) / 256;
     if (grid > (long long)cus * 8)
         grid = (long long)cus * 8;
-    const int T = (K + kTileK - 1) / kTileK;
-    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int T = (int)k_tiles(K);
+    const long long RG = row_groups(N);
     const long long items = RG * T * 16;
     const unsigned qgrid = (unsigned)((items + 255) / 256);
     hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
@@ -1487,8 +1468,8 @@ int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, int N, int K, uint8_
     if (st != NVFP4_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const int T = (K + kTileK - 1) / kTileK;
-    const long long RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int T = (int)k_tiles(K);
+    const long long RG = row_groups(N);
     const long long chunks = RG * T * 64;
     const long long items = RG * T * 16;
     hipLaunchKernelGGL(nvfp4_pack_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
@@ -1533,7 +1514,7 @@ int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const 
         return NVFP4_ERR_RANGE;
     if (ks == 0)
         ks = ksplit_for(N, K);
-    const int T = (K + kTileK - 1) / kTileK;
+    const int T = (int)k_tiles(K);
     const int tp = (T + ks - 1) / ks;
     if (ks > T || (long long)(ks - 1) * tp >= T)
         return NVFP4_ERR_SHAPE;   // some K part would be empty
@@ -1623,8 +1604,8 @@ int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uin
     p.n = n;
     p.N = N;
     p.K = K;
-    p.T = (K + kTileK - 1) / kTileK;
-    p.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    p.T = (int)k_tiles(K);
+    p.RG = (int)row_groups(N);
     GemmKernel kern = pick_gemm(geo);
     if (!kern)
         return NVFP4_ERR_SHAPE;
@@ -1702,27 +1683,27 @@ int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves, int 
     return NVFP4_OK;
 }
 
-int nvfp4_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+int nvfp4_gemv_variant(int n, int N, int K, int ks, int *variant)
 {
-    if (!buf || !sink)
+    if (!variant)
         return NVFP4_ERR_NULL;
-    if (bytes == 0 || bytes % 16 != 0)
+    if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1 || ks < 0 || ks > kMaxKParts)
         return NVFP4_ERR_RANGE;
-    if (!aligned(buf, 16) || !aligned(sink, 4))
-        return NVFP4_ERR_ALIGN;
-    int cus = 0;
-    int st = current_device_info(&cus);
-    if (st != NVFP4_OK)
-        return st;
-    // About 40 KiB per workgroup, 256 .. 2048 workgroups (measured best on
-    // MI355X for 17 .. 47 MB buffers).
-    const size_t n16 = bytes / 16;
-    size_t grid = (bytes + 40959) / 40960;
-    grid = grid < 256 ? 256 : (grid > 2048 ? 2048 : grid);
-    const size_t chunk16 = (n16 + grid - 1) / grid;
-    hipLaunchKernelGGL(nvfp4_read_stream_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, (hipStream_t)stream,
-                       reinterpret_cast<const u32x4 *>(buf), n16, chunk16, sink);
-    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+    if (K % 16 != 0 || K > kMaxK)
+        return NVFP4_ERR_SHAPE;
+    if (ks == 0)
+        ks = ksplit_for(N, K);
+    Geometry geo;
+    if (!geometry_for(N, K, 256, ks, &geo))
+        return NVFP4_ERR_SHAPE;
+    if (!pick_kernel(n, geo.mt, geo.exact, geo.kc > 1, ks > 1))
+        return NVFP4_ERR_SHAPE;
+    variant[0] = geo.mt;
+    variant[1] = (n + 3) / 4;
+    variant[2] = geo.exact ? 1 : 0;
+    variant[3] = geo.kc;
+    variant[4] = ks;
+    return NVFP4_OK;
 }
 
 const char *nvfp4_strerror(int status)

@@ -1,6 +1,9 @@
-// Measurement aid, not part of the GEMV path: the issue rate of the two ways
-// to multiply one 16-element NVFP4 block of a 16-row group by n <= 16 decode
-// tokens on gfx950, on register data with no memory traffic.
+// libnvfp4_probes: measurement aids beside the NVFP4 decode projection, not
+// part of it (C ABI in include/nvfp4_probes.h; libnvfp4 never calls them).
+//
+// nvfp4_probe_block_rate: the issue rate of the two ways to multiply one
+// 16-element NVFP4 block of a 16-row group by n <= 16 decode tokens on gfx950,
+// on register data with no memory traffic.
 //
 //  * MFMA (what nvfp4_gemv does): two v_cvt_scalef32_pk_bf16_fp4 (4 codes of
 //    the lane's weight row -> exact bf16), one v_mfma_f32_16x16x16_bf16 with
@@ -19,19 +22,25 @@
 // tile: no block depends on the previous one, nothing can be hoisted).  A
 // compiler barrier per group keeps the VALU path's LDS reads inside the loop.
 // The outputs only feed a sink.
+//
+// nvfp4_probe_read_stream: one plain read of a buffer (the read ceiling the
+// GEMV is compared with).  nvfp4_probe_empty: a launch that does nothing (the
+// fixed cost of a launch).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <string.h>
 
 #include <type_traits>
 #include <utility>
 
-#include "../../include/nvfp4.h"
+#include "../../include/nvfp4_probes.h"
 
 namespace {
 
 typedef unsigned int u32;
 typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -169,11 +178,41 @@ ProbeKernel pick_probe_n(int path, int n)
     }
 }
 
+constexpr int kReadThreads = 1024;
+constexpr int kReadUnroll = 4;
+
+// Workgroup w reads its contiguous chunk of `chunk16` 16-byte words, four
+// non-temporal loads in flight per lane; the xor of everything read goes to
+// *sink only if it equals a value no real data produces here, so the loads
+// stay live and nothing is written in practice.
+__global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4 *buf, size_t n16, size_t chunk16,
+                                                                   unsigned *sink)
+{
+    const size_t s0 = (size_t)blockIdx.x * chunk16;
+    const size_t s1 = s0 + chunk16 < n16 ? s0 + chunk16 : n16;
+    u32 acc = 0;
+    for (size_t o = s0 + threadIdx.x; o < s1; o += (size_t)kReadThreads * kReadUnroll) {
+        u32x4 v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) {
+            const size_t q = o + (size_t)u * kReadThreads;
+            v[u] = q < s1 ? __builtin_nontemporal_load(buf + q) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == 0x9E3779B9u)
+        sink[0] = acc;
+}
+
+__global__ __launch_bounds__(512) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
 
-int nvfp4_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes, void *stream)
+int nvfp4_probe_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes, void *stream)
 {
     if (!sink)
         return NVFP4_ERR_NULL;
@@ -186,6 +225,38 @@ int nvfp4_block_rate(int path, int n, int blocks, float *sink, size_t sink_bytes
         return NVFP4_ERR_ALIGN;
     hipLaunchKernelGGL(pick_probe_n(path, n), dim3(kProbeWorkgroups), dim3(kProbeThreads), 0,
                        (hipStream_t)stream, 0x1234567u, blocks, sink);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_probe_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink)
+        return NVFP4_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0)
+        return NVFP4_ERR_RANGE;
+    if ((uintptr_t)buf % 16 != 0 || (uintptr_t)sink % 4 != 0)
+        return NVFP4_ERR_ALIGN;
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return NVFP4_ERR_DEVICE;
+    // About 40 KiB per workgroup, 256 .. 2048 workgroups (measured best on
+    // MI355X for 17 .. 47 MB buffers).
+    const size_t n16 = bytes / 16;
+    size_t grid = (bytes + 40959) / 40960;
+    grid = grid < 256 ? 256 : (grid > 2048 ? 2048 : grid);
+    const size_t chunk16 = (n16 + grid - 1) / grid;
+    hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, (hipStream_t)stream,
+                       reinterpret_cast<const u32x4 *>(buf), n16, chunk16, sink);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_probe_empty(int workgroups, void *stream)
+{
+    if (workgroups < 1 || workgroups > 65536)
+        return NVFP4_ERR_RANGE;
+    hipLaunchKernelGGL(empty_kernel, dim3((unsigned)workgroups), dim3(512), 0, (hipStream_t)stream);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

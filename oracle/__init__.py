@@ -56,33 +56,32 @@ _lib = None
 
 def configure(L):
     """Declare the C signatures on a loaded copy of the oracle library."""
-    if True:
-        L.oracle_e2m1.restype = ctypes.c_double
-        L.oracle_e2m1.argtypes = [ctypes.c_int]
-        L.oracle_e4m3.restype = ctypes.c_double
-        L.oracle_e4m3.argtypes = [ctypes.c_int]
-        L.oracle_bf16_rne.restype = ctypes.c_uint16
-        L.oracle_bf16_rne.argtypes = [ctypes.c_double]
-        L.oracle_bf16_rne_array.restype = None
-        L.oracle_bf16_rne_array.argtypes = [_f64p, ctypes.c_size_t, _u16p]
-        L.oracle_e2m1_rne_index.restype = ctypes.c_int
-        L.oracle_e2m1_rne_index.argtypes = [ctypes.c_double]
-        L.oracle_e4m3_rne.restype = ctypes.c_int
-        L.oracle_e4m3_rne.argtypes = [ctypes.c_double]
-        L.oracle_tensor_scale.restype = ctypes.c_float
-        L.oracle_tensor_scale.argtypes = [_f32p, ctypes.c_size_t]
-        L.oracle_quantize.restype = None
-        L.oracle_quantize.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, _u8p, _u8p, _f32p]
-        L.oracle_dequant.restype = None
-        L.oracle_dequant.argtypes = [_u8p, _u8p, ctypes.c_float, ctypes.c_int, ctypes.c_int, _f64p]
-        L.oracle_gemv.restype = None
-        L.oracle_gemv.argtypes = [_u8p, _u8p, ctypes.c_float, _u16p, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_int, _f64p, _f64p, ctypes.c_int]
-        L.oracle_gemv_one.restype = ctypes.c_double
-        L.oracle_gemv_one.argtypes = [_u8p, _u8p, ctypes.c_float, _u16p, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, _f64p]
-        L.oracle_num_threads.restype = ctypes.c_int
-        L.oracle_num_threads.argtypes = []
+    L.oracle_e2m1.restype = ctypes.c_double
+    L.oracle_e2m1.argtypes = [ctypes.c_int]
+    L.oracle_e4m3.restype = ctypes.c_double
+    L.oracle_e4m3.argtypes = [ctypes.c_int]
+    L.oracle_bf16_rne.restype = ctypes.c_uint16
+    L.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    L.oracle_bf16_rne_array.restype = None
+    L.oracle_bf16_rne_array.argtypes = [_f64p, ctypes.c_size_t, _u16p]
+    L.oracle_e2m1_rne_index.restype = ctypes.c_int
+    L.oracle_e2m1_rne_index.argtypes = [ctypes.c_double]
+    L.oracle_e4m3_rne.restype = ctypes.c_int
+    L.oracle_e4m3_rne.argtypes = [ctypes.c_double]
+    L.oracle_tensor_scale.restype = ctypes.c_float
+    L.oracle_tensor_scale.argtypes = [_f32p, ctypes.c_size_t]
+    L.oracle_quantize.restype = None
+    L.oracle_quantize.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, _u8p, _u8p, _f32p]
+    L.oracle_dequant.restype = None
+    L.oracle_dequant.argtypes = [_u8p, _u8p, ctypes.c_float, ctypes.c_int, ctypes.c_int, _f64p]
+    L.oracle_gemv.restype = None
+    L.oracle_gemv.argtypes = [_u8p, _u8p, ctypes.c_float, _u16p, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int, _f64p, _f64p, ctypes.c_int]
+    L.oracle_gemv_one.restype = ctypes.c_double
+    L.oracle_gemv_one.argtypes = [_u8p, _u8p, ctypes.c_float, _u16p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, _f64p]
+    L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_num_threads.argtypes = []
     return L
 
 

@@ -14,7 +14,7 @@ import torch
 
 import nvfp4_weight_only_02_amd as nv
 import oracle as O
-from nvfp4_weight_only_02_amd import inputs
+from nvfp4_weight_only_02_amd import inputs, probes
 
 pytestmark = pytest.mark.gpu
 
@@ -151,7 +151,9 @@ def test_gemv_parity_1024(n):
                                  (50, 8192), (300, 640), (2049, 96),
                                  # K split into chunks (several X slices per wave):
                                  # ragged last chunk, exact chunks, ragged K tile
-                                 (40, 8208), (64, 14336), (37, 12304)])
+                                 (40, 8208), (64, 14336), (37, 12304),
+                                 # one-pass kernels with exactly 3 and 7 tiles per wave
+                                 (4100, 3072), (2000, 7168)])
 @pytest.mark.parametrize("n", [1, 5, 16])
 def test_gemv_parity_ragged(N, K, n):
     say("gemv ragged", N, K, n)
@@ -313,16 +315,56 @@ def test_full_size_parity(name, N, K, cfg, zero_outlier, row_scale, n):
     assert_parity(Y, Yref, Aref, "%s n=%d" % (name, n))
 
 
+@pytest.fixture(scope="module")
+def out_proj():
+    say("build ssm_out_proj 5120x6144 (1% zero + 1% outlier blocks)")
+    N, K = 5120, 6144
+    W, codes, scales, g = weight_case(N, K, inputs.weight_seed(4), zero_outlier=True)
+    pw = packed_from_canonical(codes, scales, g, N, K)
+    X = inputs.activations_bf16(16, K, inputs.act_seed(4, 16))
+    Yref, Aref = O.gemv(codes, scales, g, X)
+    return pw, X, Yref, Aref
+
+
+def test_out_proj_every_n(out_proj):
+    """ssm_out_proj 5120x6144 at every n = 1..16 (each n of a quad runs its own
+    kernel instantiation): every output against the oracle, and each token
+    bit-identical with the 16-token launch."""
+    pw, X, Yref, Aref = out_proj
+    Xd = x_to_dev(X)
+    full = y_bits(nv.gemv(pw, Xd))
+    assert_parity(full, Yref, Aref, "out_proj n=16")
+    for n in range(1, 16):
+        say("out_proj n", n)
+        Y = y_bits(nv.gemv(pw, Xd[:n].contiguous()))
+        assert_parity(Y, Yref[:n], Aref[:n], "out_proj n=%d" % n)
+        assert np.array_equal(Y, full[:n]), n
+
+
+def test_gemv_sched_rejects_a_wrong_output_shape():
+    W, codes, scales, g = weight_case(1024, 1024, inputs.weight_seed(0))
+    pw = packed_from_canonical(codes, scales, g, 1024, 1024)
+    X = x_to_dev(inputs.activations_bf16(4, 1024, 5))
+    with pytest.raises(ValueError):
+        nv.gemv_sched(pw, X, [3, 1], out=torch.empty((3, 1024), dtype=torch.bfloat16, device="cuda"))
+
+
 def test_block_rate_probe_runs():
     """The MFMA-vs-VALU arithmetic-rate probe launches for every n it takes
     and writes its sink (its values carry no meaning)."""
     sink = torch.full((256 * 512,), float("nan"), dtype=torch.float32, device="cuda")
-    for path in (nv.RATE_MFMA, nv.RATE_VALU):
+    for path in (probes.RATE_MFMA, probes.RATE_VALU):
         for n in (1, 2, 4, 8, 12, 16):
             sink.fill_(float("nan"))
-            nv.block_rate(path, n, 64, sink)
+            probes.block_rate(path, n, 64, sink)
             torch.cuda.synchronize()
             assert not bool(torch.isnan(sink).all()), (path, n)
+
+
+def test_empty_launch_probe_runs():
+    for wg in (1, 256, 4096):
+        probes.empty(wg)
+    torch.cuda.synchronize()
 
 
 def test_read_stream_runs_and_leaves_data():
@@ -332,7 +374,7 @@ def test_read_stream_runs_and_leaves_data():
     buf = torch.arange((1 << 20) + 48, dtype=torch.int32, device="cuda").to(torch.uint8)
     ref = buf.clone()
     sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
-    nv.read_stream(buf, sink)
+    probes.read_stream(buf, sink)
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
     assert int(sink.item()) == 7

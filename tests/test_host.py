@@ -15,6 +15,18 @@ def test_library_exports_every_header_symbol():
     L = nv.lib()
     for name in names:
         assert hasattr(L, name), name
+    # the measurement aids live in their own library and header only
+    assert not any("probe" in name or name in ("nvfp4_block_rate", "nvfp4_read_stream") for name in names)
+    assert not hasattr(L, "nvfp4_probe_read_stream") and not hasattr(L, "nvfp4_read_stream")
+
+
+def test_probe_library_exports_every_probe_header_symbol():
+    from nvfp4_weight_only_02_amd import probes
+    names = nv.header_functions(probes.HEADER_PATH)
+    assert names == ["nvfp4_probe_block_rate", "nvfp4_probe_empty", "nvfp4_probe_read_stream"]
+    P = probes.lib()
+    for name in names:
+        assert hasattr(P, name), name
 
 
 def test_strerror_names_every_status():
@@ -139,7 +151,8 @@ def test_gemv_validation(args, status):
     ((1, 8, 8, FAKE + 2, 1 << 20), 3),            # sink misaligned
 ])
 def test_block_rate_validation(args, status):
-    assert nv.lib().nvfp4_block_rate(*args, None) == status
+    from nvfp4_weight_only_02_amd import probes
+    assert probes.lib().nvfp4_probe_block_rate(*args, None) == status
 
 
 WS = (FAKE, FAKE, 1.0, FAKE, FAKE)
@@ -265,13 +278,45 @@ def test_quantize_and_pack_validation():
     assert L.nvfp4_pack(FAKE, FAKE, 16, 20, FAKE, FAKE, None) == 4
 
 
-def test_read_stream_validation():
-    L = nv.lib()
-    assert L.nvfp4_read_stream(None, 1024, FAKE, None) == 1
-    assert L.nvfp4_read_stream(FAKE, 1024, None, None) == 1
-    assert L.nvfp4_read_stream(FAKE, 0, FAKE, None) == 2
-    assert L.nvfp4_read_stream(FAKE, 1000, FAKE, None) == 2
-    assert L.nvfp4_read_stream(FAKE + 8, 1024, FAKE, None) == 3
+def test_probe_validation():
+    from nvfp4_weight_only_02_amd import probes
+    P = probes.lib()
+    assert P.nvfp4_probe_read_stream(None, 1024, FAKE, None) == 1
+    assert P.nvfp4_probe_read_stream(FAKE, 1024, None, None) == 1
+    assert P.nvfp4_probe_read_stream(FAKE, 0, FAKE, None) == 2
+    assert P.nvfp4_probe_read_stream(FAKE, 1000, FAKE, None) == 2
+    assert P.nvfp4_probe_read_stream(FAKE + 8, 1024, FAKE, None) == 3
+    assert P.nvfp4_probe_empty(0, None) == 2
+    assert P.nvfp4_probe_empty(65537, None) == 2
+
+
+def test_row_counts_near_int_max_do_not_overflow():
+    """Row groups are rounded up in 64-bit arithmetic: N = INT_MAX has
+    2^27 sixteen-row groups, and the host functions stay defined there."""
+    big = 2**31 - 1
+    assert nv.packed_codes_bytes(big, 128) == 2**27 * 16 * 64
+    assert nv.packed_scales_bytes(big, 128) == 2**27 * 16 * 8
+    wg, waves, tpw = nv.launch_geometry(1, big, 128)
+    assert wg == 256 and waves == 8 and tpw == 1
+    assert nv.gemv_variant(1, big, 128) == (1, 1, 0, 1, 1)
+    assert nv.gemv_kparts(big, 17408) >= 1
+
+
+def test_gemv_sched_checks_the_output_shape_before_the_library(monkeypatch):
+    """An output of the wrong shape is refused on the host, before the C call
+    (which could not know the buffer's size)."""
+    import torch
+
+    def no_lib():
+        raise AssertionError("the library must not be called")
+    monkeypatch.setattr(nv, "_dev", lambda t, dtype, name: t)
+    monkeypatch.setattr(nv, "lib", no_lib)
+    w = nv.PackedWeight(torch.zeros(512, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8), 1.0, 16, 64)
+    X = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out must be"):
+        nv.gemv_sched(w, X, [3, 1], out=torch.zeros((3, 16), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        nv.gemv(w, X, out=torch.zeros((4, 17), dtype=torch.bfloat16))
 
 
 def test_build_refuses_spilling_gemv_kernels():
