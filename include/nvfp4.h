@@ -58,7 +58,8 @@ typedef enum {
     NVFP4_ERR_SCHEDULE = 5,  /* an explicit tile schedule is invalid            */
     NVFP4_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch               */
     NVFP4_ERR_DEVICE = 7,    /* the current device is not a gfx950 GPU          */
-    NVFP4_ERR_WORKSPACE = 8  /* a required workspace is NULL or too small       */
+    NVFP4_ERR_WORKSPACE = 8, /* a required workspace is NULL or too small       */
+    NVFP4_ERR_SCRATCH = 9    /* beyond the fixed scratch of nvfp4_gemv_ws_static */
 } nvfp4_status;
 
 /* Largest number of tokens one launch covers (the decode batch of the pages:
@@ -154,6 +155,29 @@ int nvfp4_gemv(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
 int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
                   const uint16_t *X, uint16_t *Y, int n, int N, int K, int ks,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* nvfp4_gemv_ws for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as nvfp4_gemv_ws, except
+ * that the fp32 partials go to a fixed scratch array inside the library
+ * instead of a caller workspace: nvfp4_gemv_static_scratch_bytes() bytes
+ * (8 MiB) of device memory per GPU the library runs on, held until the
+ * process ends.  Its address on a device is looked up on the first call with
+ * ks > 1 on that device (make that first call outside graph capture); no call
+ * allocates or frees anything.  Every element the reduction reads is written
+ * earlier in the same call, so nothing needs clearing between calls.  All
+ * calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results; calls ordered on one
+ * stream are safe.  Errors: as nvfp4_gemv_ws (no WORKSPACE), SCRATCH when
+ * ks * n * N * 4 bytes exceed the scratch (checked before any HIP call),
+ * DEVICE if the scratch address cannot be looked up. */
+int nvfp4_gemv_ws_static(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
+                         const uint16_t *X, uint16_t *Y, int n, int N, int K, int ks,
+                         void *stream);
+
+/* Bytes of the fixed scratch nvfp4_gemv_ws_static uses (8 MiB).  Pure host
+ * function. */
+size_t nvfp4_gemv_static_scratch_bytes(void);
 
 /* K parts nvfp4_gemv_ws takes for ks = 0, from the shape alone: 1 while K <=
  * 8192 (one pass of the 8 waves' X slices); beyond, the part count that

@@ -25,7 +25,7 @@ MAX_TOKENS = 16
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_RANGE", 3: "NVFP4_ERR_ALIGN",
           4: "NVFP4_ERR_SHAPE", 5: "NVFP4_ERR_SCHEDULE", 6: "NVFP4_ERR_LAUNCH",
-          7: "NVFP4_ERR_DEVICE", 8: "NVFP4_ERR_WORKSPACE"}
+          7: "NVFP4_ERR_DEVICE", 8: "NVFP4_ERR_WORKSPACE", 9: "NVFP4_ERR_SCRATCH"}
 
 
 class Nvfp4Error(RuntimeError):
@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemv_ws.restype = _i32
         L.nvfp4_gemv_ws.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _vp, ctypes.c_size_t, _vp]
+        L.nvfp4_gemv_ws_static.restype = _i32
+        L.nvfp4_gemv_ws_static.argtypes = [_vp, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+        L.nvfp4_gemv_static_scratch_bytes.restype = ctypes.c_size_t
+        L.nvfp4_gemv_static_scratch_bytes.argtypes = []
         L.nvfp4_gemv_kparts.restype = _i32
         L.nvfp4_gemv_kparts.argtypes = [_i32, _i32]
         L.nvfp4_gemv_workspace_bytes.restype = ctypes.c_size_t
@@ -298,6 +302,27 @@ def gemv_ws(w: PackedWeight, X: torch.Tensor, ks: int = 0, workspace: torch.Tens
                                Y.data_ptr(), n, w.N, w.K, int(ks), workspace.data_ptr(),
                                workspace.numel(), _stream(stream)), "nvfp4_gemv_ws")
     return Y
+
+
+def gemv_ws_static(w: PackedWeight, X: torch.Tensor, ks: int = 0, out: torch.Tensor = None,
+                   stream=None) -> torch.Tensor:
+    """gemv_ws with the partials in the library's fixed scratch memory: no
+    device allocation by the library (``out`` may be given to avoid torch's).
+    Calls that overlap on one GPU race."""
+    _x(X, w.K)
+    n = X.shape[0]
+    Y = out if out is not None else torch.empty((n, w.N), dtype=torch.bfloat16, device=X.device)
+    _dev(Y, torch.bfloat16, "out")
+    if Y.shape != (n, w.N):
+        raise ValueError("out must be [n, N]")
+    _check(lib().nvfp4_gemv_ws_static(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
+                                      Y.data_ptr(), n, w.N, w.K, int(ks), _stream(stream)),
+           "nvfp4_gemv_ws_static")
+    return Y
+
+
+def gemv_static_scratch_bytes() -> int:
+    return int(lib().nvfp4_gemv_static_scratch_bytes())
 
 
 def gemv_sched(w: PackedWeight, X: torch.Tensor, tile_widths, out: torch.Tensor = None,

@@ -1152,6 +1152,33 @@ int ksplit_for(int N, int K)
     return best;
 }
 
+// Fixed device memory for callers that cannot allocate (nvfp4_gemv_ws_static):
+// the K-part partials live in this file-scope array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is only the symbol's host-side
+// stand-in: kernels get the device address hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+int scratch_on_current_device(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return NVFP4_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return NVFP4_ERR_DEVICE;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return NVFP4_OK;
+}
+
 bool aligned(const void *p, size_t a)
 {
     return ((uintptr_t)p % a) == 0;
@@ -1356,6 +1383,27 @@ int check_schedule(int n, const uint8_t *tile_widths, int ntiles)
     return sum == n ? NVFP4_OK : NVFP4_ERR_SCHEDULE;
 }
 
+// Arguments of a K-part call (nvfp4_gemv_ws, nvfp4_gemv_ws_static); *ks = 0
+// becomes the part count for the shape.
+int validate_kparts(const uint8_t *Wq, const uint8_t *Wscale, const uint16_t *X, const uint16_t *Y, int n,
+                    int N, int K, int *ks)
+{
+    int st = validate_common(Wq, Wscale, X, Y, n, N, K);
+    if (st != NVFP4_OK)
+        return st;
+    if (*ks < 0 || *ks > kMaxKParts)
+        return NVFP4_ERR_RANGE;
+    if (*ks == 0)
+        *ks = ksplit_for(N, K);
+    const int T = (int)k_tiles(K);
+    const int tp = (T + *ks - 1) / *ks;
+    if (*ks > T || (long long)(*ks - 1) * tp >= T)
+        return NVFP4_ERR_SHAPE;   // some K part would be empty
+    if (*ks > 1 && tp > kWaves * kMaxTilesPerWave)
+        return NVFP4_ERR_SHAPE;   // a K part longer than one pass (8192 columns)
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1507,19 +1555,9 @@ size_t nvfp4_gemv_workspace_bytes(int n, int N, int K, int ks)
 int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X, uint16_t *Y,
                   int n, int N, int K, int ks, void *workspace, size_t workspace_bytes, void *stream)
 {
-    int st = validate_common(Wq, Wscale, X, Y, n, N, K);
+    int st = validate_kparts(Wq, Wscale, X, Y, n, N, K, &ks);
     if (st != NVFP4_OK)
         return st;
-    if (ks < 0 || ks > kMaxKParts)
-        return NVFP4_ERR_RANGE;
-    if (ks == 0)
-        ks = ksplit_for(N, K);
-    const int T = (int)k_tiles(K);
-    const int tp = (T + ks - 1) / ks;
-    if (ks > T || (long long)(ks - 1) * tp >= T)
-        return NVFP4_ERR_SHAPE;   // some K part would be empty
-    if (ks > 1 && tp > kWaves * kMaxTilesPerWave)
-        return NVFP4_ERR_SHAPE;   // a K part longer than one pass (8192 columns)
     if (ks > 1) {
         if (!workspace || workspace_bytes < ksplit_workspace_bytes(ks, n, N))
             return NVFP4_ERR_WORKSPACE;
@@ -1527,6 +1565,28 @@ int nvfp4_gemv_ws(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const 
             return NVFP4_ERR_ALIGN;
     }
     return launch_gemv(make_params(Wq, Wscale, gscale, X, Y, n, N, K), (hipStream_t)stream, ks, workspace);
+}
+
+int nvfp4_gemv_ws_static(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
+                         uint16_t *Y, int n, int N, int K, int ks, void *stream)
+{
+    int st = validate_kparts(Wq, Wscale, X, Y, n, N, K, &ks);
+    if (st != NVFP4_OK)
+        return st;
+    if (ksplit_workspace_bytes(ks, n, N) > kScratchBytes)
+        return NVFP4_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (ks > 1) {
+        st = scratch_on_current_device(&ws);
+        if (st != NVFP4_OK)
+            return st;
+    }
+    return launch_gemv(make_params(Wq, Wscale, gscale, X, Y, n, N, K), (hipStream_t)stream, ks, ws);
+}
+
+size_t nvfp4_gemv_static_scratch_bytes(void)
+{
+    return kScratchBytes;
 }
 
 int nvfp4_gemv_qkv(const uint8_t *Wq, const uint8_t *Wscale, float gscale, const uint16_t *X,
@@ -1718,6 +1778,7 @@ const char *nvfp4_strerror(int status)
     case NVFP4_ERR_LAUNCH: return "kernel launch failed";
     case NVFP4_ERR_DEVICE: return "current device is not gfx950";
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_SCRATCH: return "call needs more than the library's fixed scratch memory";
     default: return "unknown status";
     }
 }

@@ -278,6 +278,21 @@ def test_quantize_and_pack_validation():
     assert L.nvfp4_pack(FAKE, FAKE, 16, 20, FAKE, FAKE, None) == 4
 
 
+def test_gemv_ws_static_validation():
+    """The no-allocation K-part entry point refuses, before any HIP call,
+    what does not fit its fixed 8 MiB scratch, and validates as gemv_ws."""
+    L = nv.lib()
+    assert nv.gemv_static_scratch_bytes() == 8 << 20
+    # 16 tokens x 65536 rows x 4 parts x 4 bytes = 16 MiB > 8 MiB
+    assert L.nvfp4_gemv_ws_static(FAKE, FAKE, 1.0, FAKE, FAKE, 16, 65536, 17408, 4, None) == 9
+    assert L.nvfp4_gemv_ws_static(FAKE, FAKE, 1.0, FAKE, FAKE, 16, 32768, 17408, 5, None) == 9
+    assert L.nvfp4_gemv_ws_static(0, FAKE, 1.0, FAKE, FAKE, 1, 16, 17408, 4, None) == 1
+    assert L.nvfp4_gemv_ws_static(FAKE, FAKE, 1.0, FAKE, FAKE, 17, 16, 17408, 4, None) == 2
+    assert L.nvfp4_gemv_ws_static(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 17408, 65, None) == 2
+    assert L.nvfp4_gemv_ws_static(FAKE, FAKE, 1.0, FAKE, FAKE, 1, 16, 17408, 2, None) == 4
+    assert nv.strerror(9) != "unknown status"
+
+
 def test_probe_validation():
     from nvfp4_weight_only_02_amd import probes
     P = probes.lib()
