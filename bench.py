@@ -96,7 +96,7 @@ PAGES_CONTEXT = {
 }
 METRIC = "effective weight GB/s (% of HBM peak) and GEMV-tokens/s vs n=1..16"
 SUMMARY_MAX_BYTES = 4096   # the last stdout line stays within this
-SETTLE_S = 0.03
+SETTLE_S = 0.1
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_02_amd", "csrc", "nvfp4.hip")
 
