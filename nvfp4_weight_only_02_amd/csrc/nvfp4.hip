@@ -29,12 +29,17 @@
 //  * Persistent workgroups, 8 waves each, one contiguous range of row groups
 //    per workgroup with the ranges as even as the chip allows (every
 //    workgroup runs the same number of rounds).  Each wave owns a fixed
-//    K-slice; its slice of X sits in VGPRs for the whole launch (loaded once,
-//    straight in MFMA A-operand layout, load instructions for token rows >= n
+//    K-slice, every 8th 128-column tile (wave w: tiles w, w+8, w+16, ...);
+//    its slice of X sits in VGPRs for the whole launch (loaded once, straight
+//    in MFMA A-operand layout, load instructions for token rows >= n
 //    skipped), and it streams the weight tiles of its slice for consecutive
 //    16-row groups, refilling each ring slot with the next row group's tile as
 //    soon as it is consumed (a ring of one row group: measured faster than
 //    deeper rings, whose loads return later and stall the compute behind them).
+//    With interleaved slices the refills the 8 waves issue while they work
+//    through a row group walk the next row group's tiles in ascending address
+//    order (measured faster than contiguous slices, whose refills stride the
+//    row group, at large n where the compute spreads them out).
 //  * K-slice partials are summed through LDS in a fixed wave order, then
 //    scaled by gscale and rounded to bf16 (RNE) in the epilogue, which writes
 //    each projection's rows straight to its output offset (fused QKV).
@@ -173,7 +178,9 @@ __device__ __forceinline__ void vm_wait1(u32x4 &a, std::integral_constant<int, N
 }
 
 // One launch covers every token (n <= 16) of one weight matrix.
-//   MT    tiles of the K-slice each of the kWaves waves owns in one K chunk;
+//   MT    tiles of the K-slice each of the kWaves waves owns in one K chunk
+//         (wave w: tiles cb + w + kWaves * t, t < MT, of the chunk that
+//         starts at tile cb);
 //   NV    ceil(n / 4): accumulator components that carry real tokens;
 //   EXACT every wave owns exactly MT tiles of every chunk (of every K part)
 //         (K == 128 * T, T == ks * tp, tp == kc * kWaves * MT), so no column
@@ -201,7 +208,12 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     const int pt1 = SPLIT ? min(p.T, pt0 + p.tp) : p.T;
     const int rg0 = wg * p.rg_base + min(wg, p.rg_rem);
     const int rg1 = rg0 + p.rg_base + (wg < p.rg_rem ? 1 : 0);
-    int tw0 = pt0 + wave * MT;   // first tile of this wave's slice in the current K chunk
+    // Wave w's slice of the K chunk that starts at tile cb: tiles w0 + W * t
+    // (w0 = cb + w, t < MT), of which those before the part's end pt1 exist
+    // (a prefix, since the tiles ascend with t).
+    auto first_tile = [&](int cb) { return cb + wave; };
+    auto tiles_in = [&](int w0) { return max(0, min(MT, (pt1 - w0 + W - 1) / W)); };
+    int tw0 = first_tile(pt0);   // first tile of this wave's slice in the current K chunk
     int tw = MT;                 // tiles of it that exist
 
     // All vector-memory loads of the main path are inline buffer loads waited
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 xg[t][q] = z4;
                 if (q < NV) {
                     const int row = q * 4 + (lane >> 4);
-                    const int k = (tw0 + t) * kTileK + chunk * 8;
+                    const int k = (tw0 + t * W) * kTileK + chunk * 8;
                     const bool ok = row < p.n && (EXACT || ((!SPLIT || t < tw) && k < p.K));
                     xg[t][q] = buffer_load_b128(xrsrc, ok ? (unsigned)(row * p.K + k) * 2u : kOutOfRange);
                 }
@@ -245,17 +257,19 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
     };
 
     // Weight ring: one row group of this wave's K-slice, issued as
-    // [scale chunk, code tile 0 .. MT-1].  The scale chunk is the MT * 128
-    // contiguous scale bytes of the slice (lane l holds bytes 16l .. 16l+15).
+    // [scale chunk, code tile 0 .. MT-1].  The scale chunk is the 128 scale
+    // bytes of each tile of the slice (lane l holds bytes 16(l%8) .. +15 of
+    // local tile l/8), so local tile t's scales land at bytes 128t .. 128t+127.
     u32x4 wsc;
     u32x4 wc[MT];
-    // Offsets of row group rgl of the K-slice that starts at tile w0 and
-    // holds wn tiles.
+    // Offsets of row group rgl of the K-slice whose first tile is w0 and
+    // which holds wn tiles (w0, w0 + W, ...).
     auto scale_off_at = [&](int rgl, int w0, int wn) -> unsigned {
-        return lane < 8 * wn ? (unsigned)((rgl * p.T + w0) * 128 + lane * 16) : kOutOfRange;
+        return lane < 8 * wn ? (unsigned)((rgl * p.T + w0 + (lane >> 3) * W) * 128 + (lane & 7) * 16)
+                             : kOutOfRange;
     };
     auto code_off_at = [&](int rgl, int t, int w0, int wn) -> unsigned {
-        return (EXACT || t < wn) ? (unsigned)((rgl * p.T + w0 + t) * 1024 + lane * 16) : kOutOfRange;
+        return (EXACT || t < wn) ? (unsigned)((rgl * p.T + w0 + t * W) * 1024 + lane * 16) : kOutOfRange;
     };
     auto scale_off = [&](int rgl) -> unsigned { return scale_off_at(rgl, tw0, tw); };
     auto code_off = [&](int rgl, int t) -> unsigned { return code_off_at(rgl, t, tw0, tw); };
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         // ring; after the last item the refill offsets lie past the buffer
         // resources (loads that read nothing) and are drained at the end.
         int b0 = rg0, b1 = min(rg0 + kSlots, rg1), c = 0, rg = rg0;
-        tw = EXACT ? MT : max(0, min(MT, pt1 - tw0));
+        tw = EXACT ? MT : tiles_in(tw0);
         issue_x();
         issue_ring(0);
         stage_x(std::false_type{});
@@ -459,8 +473,8 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
                 }
             }
             const bool more = nb0 < rg1;
-            const int nw0 = pt0 + (nc * W + wave) * MT;
-            const int nwn = more ? (EXACT ? MT : max(0, min(MT, pt1 - nw0))) : 0;
+            const int nw0 = first_tile(pt0 + nc * W * MT);
+            const int nwn = more ? (EXACT ? MT : tiles_in(nw0)) : 0;
             park(rg - b0, c, rowgroup(std::true_type{}, rg, more ? nrg - rg0 : rg1 - rg0, nw0, nwn));
             if (rg == b1 - 1 && c == p.kc - 1)
                 batch_end(b0, b1);
@@ -483,7 +497,7 @@ __global__ __launch_bounds__(kWaves * 64) void nvfp4_gemv_kernel(GemvParams p)
         // One K chunk: X is loaded and staged once for the whole launch, and
         // the ring runs on across batches (each slot refilled with the next
         // row group whatever batch it belongs to).
-        tw = EXACT ? MT : max(0, min(MT, pt1 - tw0));
+        tw = EXACT ? MT : tiles_in(tw0);
         issue_x();
         issue_ring(0);
         stage_x(std::false_type{});
