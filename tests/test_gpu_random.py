@@ -113,3 +113,41 @@ def test_random_fused_qkv_splits(seed):
         mask[off[p]:off[p] + rows[p]] = False
         start += rows[p]
     assert (O.bf16_bits_to_f64(Y[:, mask]) == 5.0).all()
+
+
+def big_shapes(seed, count):
+    """Row counts that give every workgroup several row groups (the ring refills
+    between them), with K drawn like shapes()."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for N0, K0, s in shapes(seed + 1, count):
+        N = int(rng.integers(4000, 12000))
+        out.append((N, K0, s))
+    return out
+
+
+@pytest.mark.parametrize("N,K,seed", big_shapes(4048, 16))
+def test_random_multi_rowgroup(N, K, seed):
+    """One-launch and K-part GEMV on N rows spread as 1-3 row groups per
+    workgroup, checked on a sample of rows: every 16-row group of the first and
+    last workgroup-sized stretch and a stride through the rest."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 17))
+    say("random multi-rowgroup", N, K, n)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x28, 0x48, size=(N, K // 16), dtype=np.uint8)
+    g = 1.0 / 128
+    pw = nv.PackedWeight.from_canonical(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                        g, N, K)
+    X = inputs.activations_bf16(n, K, seed % 77777, row_scale=bool(rng.integers(0, 2)))
+    rows = np.array(sorted(set(list(range(0, min(N, 160))) + list(range(max(0, N - 160), N))
+                           + list(range(0, N, 37)))))
+    Yref, Aref = O.gemv(np.ascontiguousarray(codes[rows]), np.ascontiguousarray(scales[rows]), g, X)
+    Y = y_bits(nv.gemv(pw, x_to_dev(X)))
+    check(Y[:, rows], Yref, Aref, "gemv %dx%d n=%d" % (N, K, n))
+    T = -(-K // 128)
+    valid = [k for k in range(2, min(T, 64) + 1) if (k - 1) * -(-T // k) < T and -(-T // k) <= 64]
+    if valid:
+        ks = int(valid[int(rng.integers(0, len(valid)))])
+        Yk = y_bits(nv.gemv_ws(pw, x_to_dev(X), ks))
+        check(Yk[:, rows], Yref, Aref, "gemv_ws %dx%d n=%d ks=%d" % (N, K, n, ks))
