@@ -3,7 +3,10 @@
 ``python -m nvfp4_weight_only_02_amd.build`` compiles libnvfp4.so (the decode
 projection, C ABI in include/nvfp4.h) and libnvfp4_probes.so (measurement
 aids beside it, include/nvfp4_probes.h).  The flags keep hipcc from emitting
-packed-fp32 VALU instructions (``-packed-fp32-ops``) for every kernel.
+packed-fp32 VALU instructions (``-packed-fp32-ops``) for every kernel.  A
+build of libnvfp4.so is refused if a GEMV or GEMM kernel spills or uses
+scratch, or if its disassembly shows a register of an in-flight load touched
+before the wait that covers the load (asmcheck.py).
 """
 from __future__ import annotations
 
@@ -64,6 +67,22 @@ def check_resources(remarks: str) -> None:
         raise RuntimeError("GEMV/GEMM kernels must not spill or use scratch:\n  " + "\n  ".join(bad))
 
 
+def check_inflight(lib: str) -> None:
+    """Refuse a build in which any GEMV or GEMM kernel names a register that a
+    vector-memory load may still be writing (asmcheck.py: a dataflow over the
+    disassembly of the gfx950 code just built).  The kernels' hand-counted
+    vmcnt waits are only right if the compiler keeps every such register
+    untouched until the wait that covers its load."""
+    from . import asmcheck   # noqa: PLC0415 (build.py also runs as a script)
+    found = {k: v for k, v in asmcheck.check_library(lib).items() if v}
+    if found:
+        lines = []
+        for kernel, hits in sorted(found.items()):
+            for addr, text, regs in hits[:3]:
+                lines.append("%s +%#x: %s (in flight: %s)" % (kernel, addr, text, regs[:4]))
+        raise RuntimeError("registers of in-flight loads are touched before their wait:\n  " + "\n  ".join(lines))
+
+
 def build_one(lib: str, sources: list, verbose: bool = False) -> str:
     """Compile one library (always) and return its path."""
     tmp = lib + ".tmp%d" % os.getpid()
@@ -88,6 +107,8 @@ def build_one(lib: str, sources: list, verbose: bool = False) -> str:
         check_resources("\n".join(lines))
         if res.returncode != 0:
             raise RuntimeError("hipcc failed:\n" + out)
+        if lib == LIB:
+            check_inflight(tmp)
     except RuntimeError:
         if os.path.exists(tmp):
             os.remove(tmp)

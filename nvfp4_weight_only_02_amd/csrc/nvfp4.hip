@@ -684,10 +684,14 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
         }
     };
     // Wait until the loads of slot q are in (the P - 1 newer steps' loads may
-    // still be in flight), then move its X into LDS buffer `buf`.
-    auto land = [&](auto slot_c, int buf) {
+    // still be in flight; with DRAIN, wait for every load), then move its X
+    // into LDS buffer `buf`.
+    auto land = [&](auto slot_c, int buf, auto drain_c) {
         constexpr int q = decltype(slot_c)::value;
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * L) : "memory");
+        if constexpr (decltype(drain_c)::value)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * L) : "memory");
 #pragma unroll
         for (int u = 0; u < XL; ++u)
             asm volatile("" : "+v"(xg[q][u]));
@@ -746,22 +750,51 @@ __global__ __launch_bounds__(GW * 64) void nvfp4_gemm_kernel(GemmParams p)
     static_assert(RGW == 1 || GW == 8, "row tiles: 1 row group per wave, or 8 waves x 2");
     auto compute = [&](auto slot_c, int buf) { compute_pipe(slot_c, buf); };
 
+    // K step s: compute from slot s % P, refill that slot with step s + P
+    // (loads past the last step read nothing), land slot (s + 1) % P.  Whole
+    // rounds of P steps run unguarded; the last T % P steps follow with
+    // nested guards, no refills, and waits for every load in flight.  So the
+    // code has no path on which a wait's count would not hold (no skipped
+    // step is followed by a taken one, the loop's back edge follows a whole
+    // round), which the build's static check of the wait counts relies on.
+    auto step = [&](auto qc, int s) {
+        constexpr int q = decltype(qc)::value;
+        compute(qc, s & 1);
+        issue(qc, s + P);
+        land(std::integral_constant<int, (q + 1) % P>{}, (s + 1) & 1, std::false_type{});
+        __syncthreads();
+    };
     static_for<P>([&](auto qc) { issue(qc, decltype(qc)::value); });
-    land(std::integral_constant<int, 0>{}, 0);
+    land(std::integral_constant<int, 0>{}, 0, std::false_type{});
     __syncthreads();
-    for (int s0 = 0; s0 < p.T; s0 += P) {
-        static_for<P>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const int s = s0 + q;
-            if (s < p.T) {
-                compute(qc, s & 1);
-                issue(qc, s + P);
-                land(std::integral_constant<int, (q + 1) % P>{}, (s + 1) & 1);
+    int s0 = 0;
+    for (; s0 + P <= p.T; s0 += P)
+        static_for<P>([&](auto qc) { step(qc, s0 + decltype(qc)::value); });
+    auto tail = [&](auto self, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q < P - 1) {
+            if (s0 + q < p.T) {
+                compute(qc, (s0 + q) & 1);
+                land(std::integral_constant<int, q + 1>{}, (s0 + q + 1) & 1, std::true_type{});
                 __syncthreads();
+                self(self, std::integral_constant<int, q + 1>{});
             }
-        });
+        }
+    };
+    tail(tail, std::integral_constant<int, 0>{});
+    // Drain the last round's loads (they read nothing).  The slot registers
+    // are used after the wait, so the compiler cannot hand them to other
+    // values while those loads may still write them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+#pragma unroll
+        for (int u = 0; u < XL; ++u)
+            asm volatile("" : "+v"(xg[q][u]));
+#pragma unroll
+        for (int r = 0; r < RGW; ++r)
+            asm volatile("" : "+v"(cw[q][r]), "+v"(sw[q][r]));
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's trailing loads read nothing
 
     // Component v of lane (g, i) of acc[r][tb]: token tok0 + 16*(wtb0 + tb) +
     // 4*g + v, weight row 16*(rgw0 + r) + i.
