@@ -54,14 +54,15 @@ int nvfp4_probe_block_rate(int path, int n, int blocks, float *sink, size_t sink
 
 /* Reads `bytes` bytes of `buf` (DEVICE, 16-byte aligned, bytes a positive
  * multiple of 16) once with the streaming pattern that reads fastest on
- * MI355X (1024-thread workgroups, contiguous chunks, four 16-byte
- * non-temporal loads in flight per lane) and writes to *sink (DEVICE, 4
+ * MI355X (1024-thread workgroups over contiguous chunks of about 40 KiB, at
+ * least 256 workgroups, four 16-byte non-temporal loads in flight per lane)
+ * and writes to *sink (DEVICE, 4
  * bytes, 4-byte aligned) only if a checksum of the data equals a value the
  * benchmark's data never produces, so that no load is dead and nothing is
  * written in practice.  Timing it over the bytes of one weight gives the
  * achievable read ceiling of that size; over a buffer of 1 GiB or more, the
- * streaming rate without the per-launch ramp.  Errors: NULL, RANGE (bytes),
- * ALIGN, DEVICE, LAUNCH. */
+ * streaming rate without the per-launch ramp.  Errors: NULL, RANGE (bytes,
+ * or more than 2^31 - 1 workgroups), ALIGN, DEVICE, LAUNCH. */
 int nvfp4_probe_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* Launches `workgroups` workgroups (1 .. 65536) of 512 threads that do

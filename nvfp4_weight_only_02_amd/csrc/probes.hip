@@ -241,11 +241,14 @@ int nvfp4_probe_read_stream(const void *buf, size_t bytes, uint32_t *sink, void 
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
         strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return NVFP4_ERR_DEVICE;
-    // About 40 KiB per workgroup, 256 .. 2048 workgroups (measured best on
-    // MI355X for 17 .. 47 MB buffers).
+    // About 40 KiB per workgroup, at least 256 workgroups (measured best on
+    // MI355X from 17 MB to 1 GiB: 1 GiB reads at 6.87 TB/s this way, at 6.26
+    // TB/s with the grid capped at 2048 workgroups of 512 KiB each).
     const size_t n16 = bytes / 16;
     size_t grid = (bytes + 40959) / 40960;
-    grid = grid < 256 ? 256 : (grid > 2048 ? 2048 : grid);
+    grid = grid < 256 ? 256 : grid;
+    if (grid > 0x7FFFFFFF)
+        return NVFP4_ERR_RANGE;
     const size_t chunk16 = (n16 + grid - 1) / grid;
     hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, (hipStream_t)stream,
                        reinterpret_cast<const u32x4 *>(buf), n16, chunk16, sink);
