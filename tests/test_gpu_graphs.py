@@ -113,3 +113,33 @@ def test_chunked_gemv_in_graph():
     X = x_dev(16, K, 7302)
     Y = torch.empty((16, N), dtype=torch.bfloat16, device="cuda")
     replay_equals_eager(lambda: nv.gemv(w, X, out=Y), Y)
+
+
+def test_concurrent_streams_give_the_serial_bits():
+    """nvfp4_gemv, nvfp4_gemv_ws (each stream with its own workspace) and
+    nvfp4_gemm keep no state between calls: launched at the same time on two
+    streams (default priority), on different weights and activations, each
+    gives the bits it gives alone."""
+    wa, wb = weight(5000, 5120, 61), weight(3000, 6144, 62)
+    xa, xb = x_dev(16, 5120, 63), x_dev(9, 6144, 64)
+    xg = x_dev(40, 5120, 65)
+    alone = [y_bits(nv.gemv(wa, xa)), y_bits(nv.gemv(wb, xb)), y_bits(nv.gemv_ws(wa, xa, 4)),
+             y_bits(nv.gemv_ws(wb, xb, 3)), y_bits(nv.gemm(wa, xg))]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            y1 = nv.gemv(wa, xa)
+            y3 = nv.gemv_ws(wa, xa, 4)
+            y5 = nv.gemm(wa, xg)
+        with torch.cuda.stream(s2):
+            y2 = nv.gemv(wb, xb)
+            y4 = nv.gemv_ws(wb, xb, 3)
+        torch.cuda.synchronize()
+        outs.append([y_bits(y1), y_bits(y2), y_bits(y3), y_bits(y4), y_bits(y5)])
+    say("two streams, 3 rounds")
+    for got in outs:
+        for a, b in zip(alone, got):
+            assert np.array_equal(a, b)
