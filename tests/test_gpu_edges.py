@@ -126,3 +126,25 @@ def test_subnormal_and_zero_block_scales():
     assert_parity(y_bits(nv.gemv(pw, x_to_dev(X[:16]))), Yref[:16], Aref[:16], "gemv")
     assert_parity(y_bits(nv.gemv_ws(pw, x_to_dev(X[:16]))), Yref[:16], Aref[:16], "gemv_ws")
     assert_parity(y_bits(nv.gemm(pw, x_to_dev(X))), Yref, Aref, "gemm")
+
+
+def test_very_many_rows():
+    """N = 2^24 + 5 rows (1048577 row groups, about 4096 per workgroup, the last
+    one ragged) at K = 128: row, row-group and output offsets beyond 2^24,
+    checked on the first and last rows and a stride through the rest, and the
+    first token against the same token alone."""
+    N, K, n = (1 << 24) + 5, 128, 3
+    say("gemv %dx%d n=%d" % (N, K, n))
+    rng = np.random.default_rng(9100)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x28, 0x48, size=(N, K // 16), dtype=np.uint8)
+    g = 1.0 / 256
+    pw = nv.PackedWeight.from_canonical(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                        g, N, K)
+    X = inputs.activations_bf16(n, K, 9101)
+    Xd = x_to_dev(X)
+    full = y_bits(nv.gemv(pw, Xd))
+    rows = np.array(sorted(set(list(range(0, 64)) + list(range(N - 64, N)) + list(range(0, N, 65537)))))
+    Yref, Aref = O.gemv(np.ascontiguousarray(codes[rows]), np.ascontiguousarray(scales[rows]), g, X)
+    assert_parity(full[:, rows], Yref, Aref, "gemv %dx%d n=%d (sampled rows)" % (N, K, n))
+    assert np.array_equal(y_bits(nv.gemv(pw, Xd[:1].contiguous()))[0], full[0])
