@@ -4,6 +4,8 @@ argument validation that must fail before any HIP call."""
 import ctypes
 
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import nvfp4_weight_only_02_amd as nv
 from nvfp4_weight_only_02_amd import metrics
@@ -70,6 +72,30 @@ def test_launch_geometry_fills_the_chip():
     assert nv.launch_geometry(1, 1024, 1024) == (64, 8, 1)
     wg, waves, tpw = nv.launch_geometry(1, 37, 144)     # ragged: 3 row groups, 2 tiles
     assert wg == 3 and waves * tpw >= 2
+
+
+@settings(max_examples=400, deadline=None)
+@given(N=st.integers(1, 1 << 22), T=st.integers(1, 2048), tail=st.sampled_from([0, 16, 112]),
+       n=st.integers(1, 16))
+def test_launch_geometry_rule_holds_everywhere(N, T, tail, n):
+    """For any shape: at most one workgroup per compute unit per round, the
+    minimal number of rounds, the fewest workgroups that keep it, 8 waves, and
+    a wave's K-slice of ceil(T / 8) tiles in one pass (T <= 64) or of at most
+    7 tiles per chunk pass beyond."""
+    K = 128 * T - tail
+    if K < 16:
+        return
+    wg, waves, mt = nv.launch_geometry(n, N, K)
+    RG = -(-N // 16)
+    rounds = -(-RG // 256)
+    assert waves == 8 and 1 <= wg <= 256
+    assert -(-RG // wg) == rounds
+    assert wg == 1 or -(-RG // (wg - 1)) > rounds
+    if T <= 64:
+        assert mt == -(-T // 8)
+    else:
+        kc = -(-T // 56)
+        assert mt == -(-T // (8 * kc)) and mt <= 7
 
 
 def _kparts_by_definition(N, K):
