@@ -112,8 +112,25 @@ def _check(status: int, what: str) -> None:
         raise Nvfp4Error(status, what)
 
 
-def _stream(stream=None):
+def check_devices(devices, current: int, stream_device) -> None:
+    """The library launches on the current device, on the given stream: every
+    tensor of a call and the stream must be on that device.  Raises ValueError
+    naming the mismatch (a pure function of torch.device values)."""
+    want = torch.device("cuda", current)
+    for d in devices:
+        if d != want:
+            raise ValueError("a tensor is on %s but the library launches on the current device %s "
+                             "(select it with torch.cuda.device)" % (d, want))
+    if stream_device != want:
+        raise ValueError("the stream is on %s but the library launches on the current device %s"
+                         % (stream_device, want))
+
+
+def _stream(stream, *tensors):
+    """The HIP stream of a launch (the current stream unless one is given),
+    after checking that it and every tensor are on the current device."""
     s = stream if stream is not None else torch.cuda.current_stream()
+    check_devices([t.device for t in tensors], torch.cuda.current_device(), s.device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -190,7 +207,7 @@ def quantize(W: torch.Tensor, stream=None):
     scales = torch.empty((N, max(K // 16, 1)), dtype=torch.uint8, device=W.device)
     ts = torch.empty(2, dtype=torch.float32, device=W.device)
     _check(lib().nvfp4_quantize(W.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(),
-                                ts.data_ptr(), _stream(stream)), "nvfp4_quantize")
+                                ts.data_ptr(), _stream(stream, W)), "nvfp4_quantize")
     return codes, scales, ts
 
 
@@ -208,7 +225,7 @@ def quantize_packed(W: torch.Tensor, stream=None):
     ts = torch.empty(2, dtype=torch.float32, device=W.device)
     dtype = 0 if W.dtype == torch.float32 else 1
     _check(lib().nvfp4_quantize_packed(W.data_ptr(), dtype, N, K, cp.data_ptr(), sp.data_ptr(),
-                                       ts.data_ptr(), _stream(stream)), "nvfp4_quantize_packed")
+                                       ts.data_ptr(), _stream(stream, W)), "nvfp4_quantize_packed")
     return cp, sp, ts
 
 
@@ -221,7 +238,7 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None)
     cp = torch.empty(packed_codes_bytes(N, K), dtype=torch.uint8, device=codes.device)
     sp = torch.empty(packed_scales_bytes(N, K), dtype=torch.uint8, device=codes.device)
     _check(lib().nvfp4_pack(codes.data_ptr(), scales.data_ptr(), N, K, cp.data_ptr(),
-                            sp.data_ptr(), _stream(stream)), "nvfp4_pack")
+                            sp.data_ptr(), _stream(stream, codes, scales)), "nvfp4_pack")
     return cp, sp
 
 
@@ -266,7 +283,7 @@ def gemv(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None
     if Y.shape != (n, w.N):
         raise ValueError("out must be [n, N]")
     _check(lib().nvfp4_gemv(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
-                            Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemv")
+                            Y.data_ptr(), n, w.N, w.K, _stream(stream, w.codes, w.scales, X, Y)), "nvfp4_gemv")
     return Y
 
 
@@ -300,7 +317,8 @@ def gemv_ws(w: PackedWeight, X: torch.Tensor, ks: int = 0, workspace: torch.Tens
     _dev(workspace, torch.uint8, "workspace")
     _check(lib().nvfp4_gemv_ws(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                                Y.data_ptr(), n, w.N, w.K, int(ks), workspace.data_ptr(),
-                               workspace.numel(), _stream(stream)), "nvfp4_gemv_ws")
+                               workspace.numel(), _stream(stream, w.codes, w.scales, X, Y, workspace)),
+           "nvfp4_gemv_ws")
     return Y
 
 
@@ -316,7 +334,8 @@ def gemv_ws_static(w: PackedWeight, X: torch.Tensor, ks: int = 0, out: torch.Ten
     if Y.shape != (n, w.N):
         raise ValueError("out must be [n, N]")
     _check(lib().nvfp4_gemv_ws_static(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
-                                      Y.data_ptr(), n, w.N, w.K, int(ks), _stream(stream)),
+                                      Y.data_ptr(), n, w.N, w.K, int(ks),
+                                      _stream(stream, w.codes, w.scales, X, Y)),
            "nvfp4_gemv_ws_static")
     return Y
 
@@ -337,7 +356,7 @@ def gemv_sched(w: PackedWeight, X: torch.Tensor, tile_widths, out: torch.Tensor 
     widths = (ctypes.c_uint8 * max(len(tile_widths), 1))(*[int(v) for v in tile_widths])
     _check(lib().nvfp4_gemv_sched(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
                                   Y.data_ptr(), n, w.N, w.K, widths, len(tile_widths),
-                                  _stream(stream)), "nvfp4_gemv_sched")
+                                  _stream(stream, w.codes, w.scales, X, Y)), "nvfp4_gemv_sched")
     return Y
 
 
@@ -351,7 +370,7 @@ def gemm(w: PackedWeight, X: torch.Tensor, out: torch.Tensor = None, stream=None
     if Y.shape != (n, w.N):
         raise ValueError("out must be [n, N]")
     _check(lib().nvfp4_gemm(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
-                            Y.data_ptr(), n, w.N, w.K, _stream(stream)), "nvfp4_gemm")
+                            Y.data_ptr(), n, w.N, w.K, _stream(stream, w.codes, w.scales, X, Y)), "nvfp4_gemm")
     return Y
 
 
@@ -361,6 +380,8 @@ def gemv_qkv(w: PackedWeight, X: torch.Tensor, rows, out_off, ldy: int,
     token-major output with ``ldy`` elements per token."""
     _x(X, w.K)
     n = X.shape[0]
+    if len(rows) != 3 or len(out_off) != 3:
+        raise ValueError("rows and out_off take three entries (q, k, v)")
     if sum(rows) != w.N:
         raise ValueError("rows must sum to N")
     Y = out if out is not None else torch.empty((n, ldy), dtype=torch.bfloat16, device=X.device)
@@ -370,6 +391,7 @@ def gemv_qkv(w: PackedWeight, X: torch.Tensor, rows, out_off, ldy: int,
     r = (ctypes.c_int32 * 3)(*[int(v) for v in rows])
     o = (ctypes.c_int64 * 3)(*[int(v) for v in out_off])
     _check(lib().nvfp4_gemv_qkv(w.codes.data_ptr(), w.scales.data_ptr(), w.gscale, X.data_ptr(),
-                                Y.data_ptr(), n, w.K, r, o, int(ldy), _stream(stream)),
+                                Y.data_ptr(), n, w.K, r, o, int(ldy),
+                                _stream(stream, w.codes, w.scales, X, Y)),
            "nvfp4_gemv_qkv")
     return Y

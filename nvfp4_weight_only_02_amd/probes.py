@@ -46,14 +46,15 @@ def block_rate(path: int, n: int, blocks: int, sink: torch.Tensor, stream=None) 
     ``sink`` is a float32 device tensor of >= 256*512 elements."""
     _dev(sink, torch.float32, "sink")
     _check(lib().nvfp4_probe_block_rate(int(path), int(n), int(blocks), sink.data_ptr(), sink.numel() * 4,
-                                        _stream(stream)), "nvfp4_probe_block_rate")
+                                        _stream(stream, sink)), "nvfp4_probe_block_rate")
 
 
 def read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """Read every byte of ``buf`` once (the read ceiling of its size)."""
     _dev(buf, torch.uint8, "buf")
     _dev(sink, torch.int32, "sink")
-    _check(lib().nvfp4_probe_read_stream(buf.data_ptr(), buf.numel(), sink.data_ptr(), _stream(stream)),
+    _check(lib().nvfp4_probe_read_stream(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                                             _stream(stream, buf, sink)),
            "nvfp4_probe_read_stream")
 
 

@@ -349,6 +349,16 @@ def test_gemv_sched_rejects_a_wrong_output_shape():
         nv.gemv_sched(pw, X, [3, 1], out=torch.empty((3, 1024), dtype=torch.bfloat16, device="cuda"))
 
 
+def test_gemv_qkv_needs_three_projections():
+    W, codes, scales, g = weight_case(1024, 1024, inputs.weight_seed(0))
+    pw = packed_from_canonical(codes, scales, g, 1024, 1024)
+    X = x_to_dev(inputs.activations_bf16(4, 1024, 5))
+    with pytest.raises(ValueError):
+        nv.gemv_qkv(pw, X, (512, 512), (0, 512), 1024)
+    with pytest.raises(ValueError):
+        nv.gemv_qkv(pw, X, (512, 256, 256), (0, 512), 1024)
+
+
 def test_block_rate_probe_runs():
     """The MFMA-vs-VALU arithmetic-rate probe launches for every n it takes
     and writes its sink (its values carry no meaning)."""

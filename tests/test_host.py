@@ -377,3 +377,16 @@ def test_build_refuses_spilling_gemv_kernels():
                 "x.hip:1:1: remark:     VGPRs Spill: 16 [-Rpass]\n")
     with pytest.raises(RuntimeError, match="must not spill"):
         build.check_resources(bad)
+
+
+def test_device_rule_of_the_binding():
+    """Every tensor of a call and its stream must be on the current device,
+    where the library launches; anything else is refused before the call."""
+    import torch
+    d0, d1 = torch.device("cuda", 0), torch.device("cuda", 1)
+    nv.check_devices([d0, d0, d0], 0, d0)
+    nv.check_devices([], 0, d0)
+    for devices, current, stream_device in [([d0, d1], 0, d0), ([d1, d1], 0, d1), ([d0], 0, d1),
+                                            ([torch.device("cpu")], 0, d0), ([d1], 1, d0)]:
+        with pytest.raises(ValueError):
+            nv.check_devices(devices, current, stream_device)
