@@ -19,8 +19,10 @@
  * patterns, accumulation is fp32, Y is rounded to nearest even.
  *
  * Conventions for every entry point:
- *   - all array pointers are DEVICE pointers; calls are asynchronous on
- *     `stream` (a hipStream_t; NULL is the default stream);
+ *   - all array pointers are DEVICE pointers of the current device (the
+ *     one hipSetDevice selected), where every launch runs; calls are
+ *     asynchronous on `stream` (a hipStream_t of that device; NULL is its
+ *     default stream);
  *   - the caller allocates and owns every buffer; the GEMV entry points
  *     allocate nothing, cache no pointer and never synchronise;
  *   - arguments are validated on the host before any HIP call; a failed
