@@ -266,9 +266,9 @@ int nvfp4_gemv_variant(int n, int N, int K, int ks, int *variant);
  * (the sum over K runs in one fixed order), but it is a different rounding
  * order from nvfp4_gemv's (both within the documented fp32 error bound).
  * For n <= 16 nvfp4_gemv is the faster call: it splits K over the waves of a
- * workgroup and keeps many more weight bytes in flight (on MI355X about 10
- * against 19 us for the 14336 x 5120 fused QKV at n = 16, where nvfp4_gemm
- * runs the same 32-token tile as at n = 32).
+ * workgroup and keeps many more weight bytes in flight (on MI355X, 14336 x
+ * 5120 fused QKV at n = 16: about 10 us against 18.5 us; nvfp4_gemm takes
+ * 18.4 - 18.7 us at any n <= 16, where it runs the 32-token tile).
  * Errors: NULL, RANGE (n, N, K), SHAPE (K % 16, K > 262144), ALIGN (Wq,
  * Wscale, X 16-byte; Y 2-byte), DEVICE, LAUNCH. */
 int nvfp4_gemm(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
