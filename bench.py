@@ -482,6 +482,28 @@ def decode_step(nv, torch, n=16):
             "timing": "20 replays of a HIP graph of the 64 launches of one step"}
 
 
+def x_staging(torch, K=5120, ns=(1, 16), reps=16):
+    """The GEMV's activation staging alone (nvfp4_probe_x_stage) at the
+    headline's K on 256 workgroups of 8 waves, X resident in L2 after the
+    first repetition: the loads alone and with the LDS round trip into the
+    MFMA layout, per staging on every compute unit (the empty launch taken
+    off), and the L2-to-compute-unit rate per XCD the loads imply (32 compute
+    units per XCD, each reading all of X)."""
+    from nvfp4_weight_only_02_amd import probes
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    empty = time_calls(torch, lambda i: probes.empty(256), 32, replays=8).mean
+    out = {"K": K, "workgroups": 256, "stagings_per_launch": reps, "empty_launch_us": round(empty * 1e6, 3)}
+    for n in ns:
+        X = make_x(torch, n, K, 2600 + n)
+        row = {"bytes_per_cu": n * K * 2}
+        for name, mode in (("loads", probes.XSTAGE_LOADS), ("full", probes.XSTAGE_FULL)):
+            tm = time_calls(torch, lambda i: probes.x_stage(X, 256, reps, mode, sink), 16, replays=6)
+            row[name + "_us"] = round((tm.mean - empty) / reps * 1e6, 3)
+        row["l2_TBps_per_xcd_loads"] = round(32 * row["bytes_per_cu"] / (row["loads_us"] * 1e-6) / 1e12, 2)
+        out["n%d" % n] = row
+    return out
+
+
 def arith_rate(torch, blocks=8192, reps=5):
     """Per-block arithmetic rate of the MFMA and VALU forms (probe library,
     register data on every SIMD, two waves each), and what it implies for the
@@ -660,6 +682,8 @@ def main():
                     help="time the headline with each allocation of the rotation copies, then exit")
     ap.add_argument("--arith-only", action="store_true",
                     help="run only the MFMA-vs-VALU arithmetic-rate probe and exit")
+    ap.add_argument("--x-stage-only", action="store_true",
+                    help="run only the activation-staging probe and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -683,6 +707,9 @@ def main():
         return
     if args.arith_only:
         print(json.dumps({"arith_rate": arith_rate(torch)}), flush=True)
+        return
+    if args.x_stage_only:
+        print(json.dumps({"x_staging": x_staging(torch)}), flush=True)
         return
     N, K = SHAPES[args.workload]
     n = args.n
@@ -919,6 +946,8 @@ def main():
 
         log("MFMA vs VALU arithmetic rate ...")
         result["arith_rate"] = arith_rate(torch)
+        log("activation staging probe ...")
+        result["x_staging"] = x_staging(torch)
 
         log("prefill GEMM sweep ...")
         result["prefill_fused_qkv"] = prefill_sweep(nv, torch, t_call)

@@ -10,8 +10,9 @@
  * exposed dequant time (doc comment of K64_N64_MAX_WIDE_CTAS).  These probes
  * give the MI355X counterparts: a plain read of the same bytes
  * (nvfp4_probe_read_stream), the cost of a launch that does nothing
- * (nvfp4_probe_empty) and the arithmetic rate of the per-block work on
- * register data (nvfp4_probe_block_rate).
+ * (nvfp4_probe_empty), the arithmetic rate of the per-block work on
+ * register data (nvfp4_probe_block_rate) and the time of the activation
+ * staging alone (nvfp4_probe_x_stage).
  *
  * Conventions are those of nvfp4.h: DEVICE pointers, asynchronous on `stream`
  * (a hipStream_t, NULL = default stream), validation on the host before any
@@ -64,6 +65,29 @@ int nvfp4_probe_block_rate(int path, int n, int blocks, float *sink, size_t sink
  * streaming rate without the per-launch ramp.  Errors: NULL, RANGE (bytes,
  * or more than 2^31 - 1 workgroups), ALIGN, DEVICE, LAUNCH. */
 int nvfp4_probe_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* Modes of nvfp4_probe_x_stage. */
+#define NVFP4_XSTAGE_LOADS 0   /* the activation loads alone                       */
+#define NVFP4_XSTAGE_FULL 1    /* loads, per-wave LDS tile, read-back into MFMA layout */
+
+/* The activation staging nvfp4_gemv does at the start of a launch, alone, as
+ * one more part of the launch split (spark_model::layers page, doc comment of
+ * K64_N64_MAX_WIDE_CTAS): `workgroups` workgroups of 8 waves (1 .. 65536),
+ * wave w taking the 128-column tiles w, w + 8, w + 16, ... of K for the n
+ * token rows of X (bf16 [n][K], DEVICE, 16-byte aligned) with whole-line
+ * 16-byte loads, `reps` times per launch (1 .. 1024).  NVFP4_XSTAGE_LOADS
+ * stops after the loads; NVFP4_XSTAGE_FULL also writes each tile to the
+ * wave's LDS tile and reads it back in the MFMA operand layout, as the GEMV
+ * does (only the groups of four token rows that hold a token are written,
+ * and only the lanes that carry a token read back).  Every workgroup reads the same X, so after the first repetition it
+ * comes from L2: the launch time over reps is one staging on every compute
+ * unit at once, bounded by what each XCD's L2 delivers.  n in 1 .. 16, K a
+ * multiple of 128 from 128 to 8192 (one pass of the GEMV).  *sink (DEVICE, 4
+ * bytes, 4-byte aligned) is written only if a checksum of the data equals a
+ * value the benchmark's data never produces.  Errors: NULL, RANGE, ALIGN,
+ * LAUNCH. */
+int nvfp4_probe_x_stage(const uint16_t *X, int n, int K, int workgroups, int reps, int mode,
+                        uint32_t *sink, void *stream);
 
 /* Launches `workgroups` workgroups (1 .. 65536) of 512 threads that do
  * nothing: the fixed cost of one launch of the GEMV's shape (its dispatch,

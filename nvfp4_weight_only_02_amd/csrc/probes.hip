@@ -25,7 +25,9 @@
 //
 // nvfp4_probe_read_stream: one plain read of a buffer (the read ceiling the
 // GEMV is compared with).  nvfp4_probe_empty: a launch that does nothing (the
-// fixed cost of a launch).
+// fixed cost of a launch).  nvfp4_probe_x_stage: the GEMV's staging of the
+// activations alone (the loads, or the loads plus the per-wave LDS tile and
+// the read-back into the MFMA operand layout), repeated inside one launch.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -208,6 +210,103 @@ __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4 *
 
 __global__ __launch_bounds__(512) void empty_kernel() {}
 
+// The activation staging of nvfp4_gemv for a K-slice of MT 128-column tiles
+// per wave (wave w: tiles w, w + 8, ...), `reps` times: whole-line 16-byte
+// buffer loads of the token rows of each tile (lane l: row 4q + l/16, bytes
+// 16 * (l % 16) of the tile's 256; a row beyond n or a column beyond K reads
+// nothing, as in the GEMV), then with FULL the per-wave LDS tile and the
+// read-back of each lane's MFMA A fragments (token 4(i%4) + i/4, columns
+// 16b + 4g .. +3 of block b).  As in the GEMV, only the NV = ceil(n/4) groups
+// of four token rows that hold a token are loaded and written, and only the
+// lanes whose MFMA row carries a token read back.  Everything feeds a
+// checksum that reaches *sink only for a value the benchmark's data never
+// produces.
+template <int MT, int NV, bool FULL>
+__global__ __launch_bounds__(kProbeThreads) void x_stage_kernel(const u32x4 *__restrict__ x, int n, int K,
+                                                                int reps, u32 *sink)
+{
+    // range-checked resource over X's n*K bf16 (gfx9 raw buffer word 3)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(x), (short)0,
+                                                                        n * K * 2, 0x00020000);
+    __shared__ u32x4 xs[kProbeThreads / 64][16][17];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = lane & 15, g = lane >> 4, chunk = lane & 15;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool xlane = 4 * (i & 3) + (i >> 2) < 4 * NV;
+    u32 acc = 0;
+    for (int rep = 0; rep < reps; ++rep) {
+        asm volatile("" ::: "memory");   // every repetition loads again
+        u32x4 v[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = q * 4 + (lane >> 4);
+                const int k = (w + 8 * t) * 128 + chunk * 8;
+                v[t][q] = z;
+                if (q < NV)
+                    v[t][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            xr, row < n && k < K ? (unsigned)(row * K + k) * 2u
+                                                                                 : 0x7FFFFFF0u, 0, 0));
+            }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if constexpr (!FULL) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc ^= v[t][q][0] + 3u * v[t][q][1] + 5u * v[t][q][2] + 7u * v[t][q][3];
+            } else {
+#pragma unroll
+                for (int q = 0; q < NV; ++q)
+                    xs[w][q * 4 + (lane >> 4)][chunk] = v[t][q];
+                const char *base = reinterpret_cast<const char *>(&xs[w][4 * (i & 3) + (i >> 2)][0]);
+                if (xlane) {
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) {
+                        const u32x2 r = *reinterpret_cast<const u32x2 *>(base + (16 * b + 4 * g) * 2);
+                        acc ^= r[0] + 3u * r[1];
+                    }
+                }
+            }
+        }
+    }
+    if (acc == 0x9E3779B9u)
+        sink[0] = acc;
+}
+
+typedef void (*XStageKernel)(const u32x4 *, int, int, int, u32 *);
+
+template <int MT, int NV>
+XStageKernel pick_x_stage_mode(int mode)
+{
+    return mode == NVFP4_XSTAGE_FULL ? x_stage_kernel<MT, NV, true> : x_stage_kernel<MT, NV, false>;
+}
+
+template <int MT>
+XStageKernel pick_x_stage_nv(int n, int mode)
+{
+    switch ((n + 3) / 4) {
+    case 1: return pick_x_stage_mode<MT, 1>(mode);
+    case 2: return pick_x_stage_mode<MT, 2>(mode);
+    case 3: return pick_x_stage_mode<MT, 3>(mode);
+    default: return pick_x_stage_mode<MT, 4>(mode);
+    }
+}
+
+XStageKernel pick_x_stage(int mt, int n, int mode)
+{
+    switch (mt) {
+    case 1: return pick_x_stage_nv<1>(n, mode);
+    case 2: return pick_x_stage_nv<2>(n, mode);
+    case 3: return pick_x_stage_nv<3>(n, mode);
+    case 4: return pick_x_stage_nv<4>(n, mode);
+    case 5: return pick_x_stage_nv<5>(n, mode);
+    case 6: return pick_x_stage_nv<6>(n, mode);
+    case 7: return pick_x_stage_nv<7>(n, mode);
+    default: return pick_x_stage_nv<8>(n, mode);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +351,22 @@ int nvfp4_probe_read_stream(const void *buf, size_t bytes, uint32_t *sink, void 
     const size_t chunk16 = (n16 + grid - 1) / grid;
     hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)grid), dim3(kReadThreads), 0, (hipStream_t)stream,
                        reinterpret_cast<const u32x4 *>(buf), n16, chunk16, sink);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+int nvfp4_probe_x_stage(const uint16_t *X, int n, int K, int workgroups, int reps, int mode, uint32_t *sink,
+                        void *stream)
+{
+    if (!X || !sink)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > 16 || K < 128 || K > 8192 || K % 128 != 0 || workgroups < 1 || workgroups > 65536 ||
+        reps < 1 || reps > 1024 || (mode != NVFP4_XSTAGE_LOADS && mode != NVFP4_XSTAGE_FULL))
+        return NVFP4_ERR_RANGE;
+    if ((uintptr_t)X % 16 != 0 || (uintptr_t)sink % 4 != 0)
+        return NVFP4_ERR_ALIGN;
+    const int mt = (K / 128 + 7) / 8;
+    hipLaunchKernelGGL(pick_x_stage(mt, n, mode), dim3((unsigned)workgroups), dim3(kProbeThreads), 0,
+                       (hipStream_t)stream, reinterpret_cast<const u32x4 *>(X), n, K, reps, sink);
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

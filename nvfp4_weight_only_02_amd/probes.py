@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4_probes.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "nvfp4_probes.h")
 RATE_MFMA, RATE_VALU = 0, 1
+XSTAGE_LOADS, XSTAGE_FULL = 0, 1
 
 _lib = None
 
@@ -32,6 +33,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.nvfp4_probe_empty.restype = ctypes.c_int
         L.nvfp4_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.nvfp4_probe_x_stage.restype = ctypes.c_int
+        L.nvfp4_probe_x_stage.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -61,3 +65,14 @@ def read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
 def empty(workgroups: int, stream=None) -> None:
     """A launch of ``workgroups`` 512-thread workgroups that do nothing."""
     _check(lib().nvfp4_probe_empty(int(workgroups), _stream(stream)), "nvfp4_probe_empty")
+
+
+def x_stage(X: torch.Tensor, workgroups: int, reps: int, mode: int, sink: torch.Tensor, stream=None) -> None:
+    """The GEMV's activation staging alone (XSTAGE_LOADS or XSTAGE_FULL) for
+    X bf16 [n, K], ``reps`` times per launch on ``workgroups`` workgroups."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(sink, torch.int32, "sink")
+    if X.dim() != 2:
+        raise ValueError("X must be [n, K]")
+    _check(lib().nvfp4_probe_x_stage(X.data_ptr(), X.shape[0], X.shape[1], int(workgroups), int(reps), int(mode),
+                                     sink.data_ptr(), _stream(stream, X, sink)), "nvfp4_probe_x_stage")

@@ -377,6 +377,17 @@ def test_empty_launch_probe_runs():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("mode", [probes.XSTAGE_LOADS, probes.XSTAGE_FULL])
+def test_x_stage_probe_runs_and_leaves_data(mode):
+    X = x_to_dev(inputs.activations_bf16(16, 5120, 11))
+    before = X.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    probes.x_stage(X, 256, 4, mode, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(X.view(torch.int16), before.view(torch.int16))
+    assert int(sink.item()) == 0
+
+
 def test_read_stream_runs_and_leaves_data():
     """The read-ceiling aid reads a buffer without changing it (sink written
     only on a checksum value the data below cannot produce)."""

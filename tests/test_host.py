@@ -25,7 +25,7 @@ def test_library_exports_every_header_symbol():
 def test_probe_library_exports_every_probe_header_symbol():
     from nvfp4_weight_only_02_amd import probes
     names = nv.header_functions(probes.HEADER_PATH)
-    assert names == ["nvfp4_probe_block_rate", "nvfp4_probe_empty", "nvfp4_probe_read_stream"]
+    assert names == ["nvfp4_probe_block_rate", "nvfp4_probe_empty", "nvfp4_probe_read_stream", "nvfp4_probe_x_stage"]
     P = probes.lib()
     for name in names:
         assert hasattr(P, name), name
@@ -329,6 +329,14 @@ def test_probe_validation():
     assert P.nvfp4_probe_read_stream(FAKE + 8, 1024, FAKE, None) == 3
     assert P.nvfp4_probe_empty(0, None) == 2
     assert P.nvfp4_probe_empty(65537, None) == 2
+    # nvfp4_probe_x_stage(X, n, K, workgroups, reps, mode, sink, stream)
+    assert P.nvfp4_probe_x_stage(None, 16, 5120, 256, 4, 0, FAKE, None) == 1
+    assert P.nvfp4_probe_x_stage(FAKE, 16, 5120, 256, 4, 0, None, None) == 1
+    for bad in [(0, 5120, 256, 4, 0), (17, 5120, 256, 4, 0), (16, 5000, 256, 4, 0), (16, 8320, 256, 4, 0),
+                (16, 0, 256, 4, 0), (16, 5120, 0, 4, 0), (16, 5120, 65537, 4, 0), (16, 5120, 256, 0, 0),
+                (16, 5120, 256, 1025, 0), (16, 5120, 256, 4, 2)]:
+        assert P.nvfp4_probe_x_stage(FAKE, *bad, FAKE, None) == 2, bad
+    assert P.nvfp4_probe_x_stage(FAKE + 8, 16, 5120, 256, 4, 0, FAKE, None) == 3
 
 
 def test_row_counts_near_int_max_do_not_overflow():
