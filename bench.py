@@ -45,7 +45,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -98,7 +97,7 @@ METRIC = "effective weight GB/s (% of HBM peak) and GEMV-tokens/s vs n=1..16"
 SUMMARY_MAX_BYTES = 4096   # the last stdout line stays within this
 SETTLE_S = 0.1
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_02_amd", "csrc", "nvfp4.hip")
+KERNEL_LIB = os.path.join(ROOT, "nvfp4_weight_only_02_amd", "libnvfp4.so")
 
 
 def counters_file(workload: str, n: int) -> str:
@@ -109,9 +108,23 @@ def per_n_counters_file(workload: str) -> str:
     return os.path.join(PROFILES, "gemv_%s_per_n_counters.json" % workload)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+_CODE_HASH = []
+
+
+def kernel_code_hash():
+    """sha256 prefix of the gfx950 code of every nvfp4_gemv_kernel
+    instantiation in the built libnvfp4.so (names and instructions, no
+    addresses), which stored counters must match: they were measured on
+    exactly that code, and host-side changes to the library leave it as it
+    is.  None if the library cannot be disassembled here (then no stored
+    figure is used)."""
+    if not _CODE_HASH:
+        try:
+            from nvfp4_weight_only_02_amd import asmcheck
+            _CODE_HASH.append(asmcheck.code_hash(KERNEL_LIB))
+        except Exception:
+            _CODE_HASH.append(None)
+    return _CODE_HASH[0]
 
 
 _T0 = time.perf_counter()
@@ -593,7 +606,7 @@ def cpu_baseline(N, K, n, seconds, row_scale):
 def annotate_counter_bandwidth(sweep: dict, workload: str) -> None:
     """Add the HBM bandwidth rocprofv3's FETCH_SIZE + WRITE_SIZE imply (bytes
     per launch from the committed per-n counter summary / time per call) to
-    the sweep points it covers, while that summary matches the kernel source
+    the sweep points it covers, while that summary matches the kernel code
     and the workload."""
     from nvfp4_weight_only_02_amd import metrics
     try:
@@ -601,7 +614,8 @@ def annotate_counter_bandwidth(sweep: dict, workload: str) -> None:
             c = json.load(f)
     except (OSError, ValueError):
         return
-    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != workload:
+    code = kernel_code_hash()
+    if code is None or c.get("kernel_code_sha256_16") != code or c.get("workload") != workload:
         return
     for n, b in c.get("hbm_bytes_per_launch", {}).items():
         if n in sweep:
@@ -613,13 +627,14 @@ def annotate_counter_bandwidth(sweep: dict, workload: str) -> None:
 def stored_traffic(workload: str, n: int):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None if the summary is absent, covers another workload or was taken on
-    a different kernel source."""
+    different kernel code."""
     try:
         with open(counters_file(workload, n)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != "%s n=%d" % (workload, n):
+    code = kernel_code_hash()
+    if code is None or c.get("kernel_code_sha256_16") != code or c.get("workload") != "%s n=%d" % (workload, n):
         return None
     return c.get("hbm_bytes_per_launch")
 

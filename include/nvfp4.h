@@ -222,7 +222,8 @@ int nvfp4_gemv_sched(const uint8_t *Wq, const uint8_t *Wscale, float gscale,
 
 /* The dispatcher's schedule for (n, N, K): writes the tile widths nvfp4_gemv
  * uses into widths (HOST, capacity max_tiles) and returns their count, or a
- * negative status.  Pure host function. */
+ * negative status (RANGE, SHAPE for a shape nvfp4_gemv refuses, SCHEDULE for
+ * no room).  Pure host function. */
 int nvfp4_schedule(int n, int N, int K, uint8_t *widths, int max_tiles);
 
 /* The pages' greedy schedule (Atlas PR #266 description): as many tiles of

@@ -21,6 +21,7 @@ register of an outstanding load is reported.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import re
 import shutil
@@ -224,3 +225,20 @@ def check_library(lib: str, pattern: str = r"nvfp4_gem[mv]_kernel") -> dict:
     if not names:
         raise RuntimeError("no function matching %r in %s" % (pattern, lib))
     return {f: check_function(funcs[f]) for f in names}
+
+
+def code_hash(lib: str, pattern: str = r"nvfp4_gemv_kernel") -> str:
+    """sha256 prefix (16 hex digits) of the gfx950 code of every function of
+    `lib` whose name matches `pattern`: names and instruction text in name
+    order, without addresses.  It changes with the kernels' machine code and
+    with nothing else (host code, other kernels)."""
+    funcs = parse(disassemble(lib))
+    names = sorted(f for f in funcs if re.search(pattern, f))
+    if not names:
+        raise RuntimeError("no function matching %r in %s" % (pattern, lib))
+    h = hashlib.sha256()
+    for f in names:
+        h.update(f.encode() + b"\n")
+        for _, mnem, ops in funcs[f]:
+            h.update((mnem + " " + ops + "\n").encode())
+    return h.hexdigest()[:16]

@@ -1746,6 +1746,8 @@ int nvfp4_schedule(int n, int N, int K, uint8_t *widths, int max_tiles)
         return -NVFP4_ERR_NULL;
     if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1)
         return -NVFP4_ERR_RANGE;
+    if (K % 16 != 0 || K > kMaxK)
+        return -NVFP4_ERR_SHAPE;   // a shape nvfp4_gemv refuses has no schedule
     if (max_tiles < 1)
         return -NVFP4_ERR_SCHEDULE;
     // One launch reads the weight once for every n <= 16; measured faster than
@@ -1778,7 +1780,7 @@ int nvfp4_launch_geometry(int n, int N, int K, int *workgroups, int *waves, int 
         return NVFP4_ERR_NULL;
     if (n < 1 || n > NVFP4_MAX_TOKENS || N < 1 || K < 1)
         return NVFP4_ERR_RANGE;
-    if (K % 16 != 0)
+    if (K % 16 != 0 || K > kMaxK)
         return NVFP4_ERR_SHAPE;
     int cus = 256;   // MI355X; the launch itself uses the queried count
     Geometry geo;

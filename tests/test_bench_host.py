@@ -23,16 +23,16 @@ def test_stored_traffic_only_for_its_workload_and_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     f = bench.counters_file("ssm_qkvz_16384x5120", 16)
     assert os.path.dirname(f) == str(tmp_path)
-    sha = bench.kernel_source_hash()
-    write(f, {"workload": "ssm_qkvz_16384x5120 n=16", "kernel_source_sha256_16": sha,
+    sha = bench.kernel_code_hash()
+    write(f, {"workload": "ssm_qkvz_16384x5120 n=16", "kernel_code_sha256_16": sha,
               "hbm_bytes_per_launch": 48700000})
     assert bench.stored_traffic("ssm_qkvz_16384x5120", 16) == 48700000
     assert bench.stored_traffic("ssm_qkvz_16384x5120", 8) is None           # another n: no file
     assert bench.stored_traffic("fused_qkv_14336x5120", 16) is None         # another shape: no file
-    write(f, {"workload": "fused_qkv_14336x5120 n=16", "kernel_source_sha256_16": sha,
+    write(f, {"workload": "fused_qkv_14336x5120 n=16", "kernel_code_sha256_16": sha,
               "hbm_bytes_per_launch": 48700000})
     assert bench.stored_traffic("ssm_qkvz_16384x5120", 16) is None          # file describes another workload
-    write(f, {"workload": "ssm_qkvz_16384x5120 n=16", "kernel_source_sha256_16": "0" * 16,
+    write(f, {"workload": "ssm_qkvz_16384x5120 n=16", "kernel_code_sha256_16": "0" * 16,
               "hbm_bytes_per_launch": 48700000})
     assert bench.stored_traffic("ssm_qkvz_16384x5120", 16) is None          # kernel changed since
 
@@ -40,7 +40,7 @@ def test_stored_traffic_only_for_its_workload_and_source(tmp_path, monkeypatch):
 def test_counter_bandwidth_per_n(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     write(bench.per_n_counters_file("fused_qkv_14336x5120"),
-          {"workload": "fused_qkv_14336x5120", "kernel_source_sha256_16": bench.kernel_source_hash(),
+          {"workload": "fused_qkv_14336x5120", "kernel_code_sha256_16": bench.kernel_code_hash(),
            "hbm_bytes_per_launch": {"1": 4_000_000, "16": 8_000_000}})
     sweep = {"1": {"us": 2.0}, "2": {"us": 2.0}, "16": {"us": 4.0}}
     bench.annotate_counter_bandwidth(sweep, "fused_qkv_14336x5120")
@@ -60,7 +60,7 @@ def test_committed_counter_summaries_describe_themselves():
             c = json.load(f)
         shape = re.match(r"gemv_(.+?)_(n\d+|per_n)_counters\.json$", name).group(1)
         assert c["workload"].startswith(shape), name
-        assert len(c["kernel_source_sha256_16"]) == 16
+        assert len(c["kernel_code_sha256_16"]) == 16
         assert 0.9 < c["copy_calibration_fetch_factor"] * 2 < 1.1   # a copy reads FETCH_SIZE of half its bytes
 
 

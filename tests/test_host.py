@@ -398,3 +398,62 @@ def test_device_rule_of_the_binding():
                                             ([torch.device("cpu")], 0, d0), ([d1], 1, d0)]:
         with pytest.raises(ValueError):
             nv.check_devices(devices, current, stream_device)
+
+
+@settings(max_examples=300, deadline=None)
+@given(N=st.integers(-3, 2**31 - 1), K=st.integers(-40, 300000), n=st.integers(-2, 40), ks=st.integers(-2, 80))
+def test_host_queries_are_total_and_consistent(N, K, n, ks):
+    """The pure host functions (no device, no launch) answer every argument
+    set, including sizes near INT_MAX, without overflow: packed sizes follow
+    the tile layout, the part count is 1..64 for every valid shape, the
+    workspace is parts * n * N * 4 bytes, a schedule covers exactly n tokens,
+    and geometry is reported only for shapes nvfp4_gemv accepts."""
+    L = nv.lib()
+    shape_ok = N >= 1 and 16 <= K <= 262144 and K % 16 == 0
+    cb, sb = L.nvfp4_packed_codes_bytes(N, K), L.nvfp4_packed_scales_bytes(N, K)
+    if N >= 1 and K >= 1 and K % 16 == 0:
+        rg, t = -(-N // 16), -(-K // 128)
+        assert (cb, sb) == (rg * t * 1024, rg * t * 128)
+    else:
+        assert (cb, sb) == (0, 0)
+    kp = L.nvfp4_gemv_kparts(N, K)
+    if shape_ok:
+        assert 1 <= kp <= 64
+    else:
+        assert kp < 0
+    wb = L.nvfp4_gemv_workspace_bytes(n, N, K, ks)
+    parts = kp if ks == 0 else ks
+    if shape_ok and 1 <= n <= 16 and parts > 1 and wb:
+        assert wb == parts * n * N * 4
+    if not shape_ok or not 1 <= n <= 16:
+        assert wb == 0
+    buf = (ctypes.c_uint8 * 16)()
+    cnt = L.nvfp4_schedule(n, N, K, buf, 16)
+    if 1 <= n <= 16 and shape_ok:
+        assert cnt >= 1 and sum(buf[:cnt]) == n and all(1 <= w <= 16 for w in buf[:cnt])
+    else:
+        assert cnt < 0
+    wg, wv, tpw = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    status = L.nvfp4_launch_geometry(n, N, K, ctypes.byref(wg), ctypes.byref(wv), ctypes.byref(tpw))
+    if status == 0:
+        assert shape_ok and 1 <= n <= 16
+        assert 1 <= wg.value <= 256 and wv.value == 8 and 1 <= tpw.value <= 8
+    elif shape_ok and 1 <= n <= 16:
+        assert status == 4   # SHAPE: a workgroup's codes beyond a 32-bit buffer offset
+
+
+
+def test_committed_counters_match_the_built_kernel_code():
+    """The HBM counter summaries the bench reads were taken on exactly the
+    GEMV machine code built here (else the bench would report no traffic)."""
+    import json
+    import os
+    import bench
+    code = bench.kernel_code_hash()
+    assert code is not None
+    folder = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+    names = [f for f in os.listdir(folder) if f.endswith("_counters.json")]
+    assert names
+    for name in names:
+        with open(os.path.join(folder, name)) as f:
+            assert json.load(f)["kernel_code_sha256_16"] == code, name
