@@ -457,3 +457,38 @@ def test_committed_counters_match_the_built_kernel_code():
     for name in names:
         with open(os.path.join(folder, name)) as f:
             assert json.load(f)["kernel_code_sha256_16"] == code, name
+
+
+_PTRS = st.sampled_from([None, FAKE, FAKE + 2, FAKE + 8])
+_INTS = st.one_of(st.integers(-5, 70), st.integers(-(2**31), 2**31 - 1), st.sampled_from([16, 128, 5120, 262144, 262160]))
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="arguments can pass validation: only safe where no GPU would run the launch")
+@settings(max_examples=300, deadline=None)
+@given(ptrs=st.lists(_PTRS, min_size=6, max_size=6), ints=st.lists(_INTS, min_size=8, max_size=8),
+       size=st.integers(0, 2**40))
+def test_launching_entry_points_never_crash_on_host(ptrs, ints, size):
+    """Every entry point that launches work answers any argument set with a
+    status: a validation error, or (here, with no GPU) NVFP4_ERR_DEVICE.  It
+    never returns OK without a device and never crashes on the host."""
+    L = nv.lib()
+    a, b, x, y, ws, sink = ptrs
+    n, N, K, ks, r0, r1, r2, ldy = ints
+    statuses = set(range(1, 10))
+    rows = (ctypes.c_int32 * 3)(*(max(-(2**31), min(2**31 - 1, v)) for v in (r0, r1, r2)))
+    offs = (ctypes.c_int64 * 3)(r2, r0, r1)
+    widths = (ctypes.c_uint8 * 4)(*(v & 0xFF for v in (n, ks, r0, r1)))
+    calls = [
+        L.nvfp4_gemv(a, b, 1.0, x, y, n, N, K, None),
+        L.nvfp4_gemv_ws(a, b, 1.0, x, y, n, N, K, ks, ws, size, None),
+        L.nvfp4_gemv_ws_static(a, b, 1.0, x, y, n, N, K, ks, None),
+        L.nvfp4_gemv_qkv(a, b, 1.0, x, y, n, K, rows, offs, ldy, None),
+        L.nvfp4_gemv_sched(a, b, 1.0, x, y, n, N, K, widths, ks & 3, None),
+        L.nvfp4_gemm(a, b, 1.0, x, y, n, N, K, None),
+        L.nvfp4_pack(a, b, N, K, x, y, None),
+        L.nvfp4_quantize(a, N, K, x, y, sink, None),
+        L.nvfp4_quantize_packed(a, ks & 1, N, K, x, y, sink, None),
+    ]
+    for i, status in enumerate(calls):
+        assert status in statuses, (i, status)
